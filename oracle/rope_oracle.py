@@ -1,0 +1,358 @@
+"""CPU oracle for rotary position embedding (RoPE) fused into a FlashAttention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The product
+path (the HIP library and its Python binding) never imports it, and this module
+imports nothing from the product package.
+
+Everything here is plain numpy in float64 and follows the definitions on the
+source pages, with no blocking, fusion or reordering beyond what the definitions
+state.  Page key used in the citations:
+
+* [RoPE-fusion blog]  devpress.csdn.net/awstech/6a91ac403bda720d4b352e13 — RoPE
+  fused into FlashAttention in ops-transformer (sections 1.2, 5.3).
+* [FlashAttention blog]  hwcomputing.csdn.net/6a0d3f5c662f9a54cb75d0b0 — the
+  attention formula and its three steps ("Attention 的显存坑在哪"), online softmax.
+* [DynamicNTKOperation]  hiascend.com API page ascendtb_01_0140 — sections
+  功能说明 (function), 算子功能分析 (formula), 输入/输出 (inputs/outputs),
+  约束说明 (constraints).
+* [RoPE/GQA tutorial]  smarter.xin/posts/3494b8a4 — section 五 (relative
+  position), 六 (rotation geometry), 十一/十二 (MQA/GQA).
+
+Readings taken where the pages are silent (also listed in the design notes):
+rotate-half pairing (dims i and i+D/2 share frequency i, from emb = cat(freq,
+freq)); rotation sign R = [[cos, -sin], [sin, cos]] on (x_i, x_{i+D/2});
+angles formed in float32 (int32 positions, float32 inverse frequencies);
+contiguous GQA grouping (kv head = q head // group); softmax scale passed in.
+
+Parity status: every function below is pinned by tests/test_oracle.py except
+``ntk_base``, whose formula is not on the pages (parity unpinned; only its
+"no change at or below the trained length" property is pinned).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "inv_freq",
+    "ntk_base",
+    "inv_freq_per_sequence",
+    "segment_ids",
+    "segment_starts",
+    "angles",
+    "rope_tables",
+    "rotation_matrix",
+    "rope_op_matrix",
+    "rotate_tokens",
+    "attention",
+    "rope_attention",
+    "rope_attention_rows",
+    "round_rne",
+    "ulp",
+    "DTYPE_FORMATS",
+]
+
+# (precision p incl. the implicit bit, minimum normal exponent emin)
+DTYPE_FORMATS = {"f16": (11, -14), "bf16": (8, -126), "f32": (24, -126)}
+
+
+# --------------------------------------------------------------------------- a1
+def inv_freq(base: float, head_size: int) -> np.ndarray:
+    """Inverse frequencies f_i = base^(-2i/D) for i < D/2, as float32.
+
+    [RoPE-fusion blog, section 1.2 snippet]: freqs = 1 / base ** (arange(0, D, 2) / D).
+    Formed in float64 and rounded once to float32, since the table op takes its
+    inverse frequencies as a float32 input ([DynamicNTKOperation, 输入 table]).
+    """
+    if head_size <= 0 or head_size % 2:
+        raise ValueError("head_size must be a positive even number")
+    exps = np.arange(0, head_size, 2, dtype=np.float64) / float(head_size)
+    return (1.0 / (float(base) ** exps)).astype(np.float32)
+
+
+def ntk_base(base: float, seq_len: int, trained_len: int, head_size: int) -> float:
+    """Dynamic-NTK base for one sequence.  PARITY UNPINNED (formula not on the pages).
+
+    [DynamicNTKOperation, 功能说明]: no interpolation when the inference length is at
+    most the trained length; above it the base is enlarged.  The enlargement law is
+    lost from the page (its InvFreqs formula did not survive); the reading used is
+    base * (L / L_train) ** (D / (D - 2)).
+    """
+    if seq_len <= trained_len:
+        return float(base)
+    return float(base) * (float(seq_len) / float(trained_len)) ** (float(head_size) / float(head_size - 2))
+
+
+def inv_freq_per_sequence(base: float, seq_lens, head_size: int, trained_len: int | None) -> np.ndarray:
+    """[batch, D/2] float32 inverse frequencies, one row per sequence.
+
+    [DynamicNTKOperation, 输入]: InvFreqs has shape [batch, headSize/2].  With
+    ``trained_len=None`` every row uses ``base`` (no NTK scaling).
+    """
+    rows = []
+    for L in np.asarray(seq_lens).tolist():
+        b = float(base) if trained_len is None else ntk_base(base, int(L), int(trained_len), head_size)
+        rows.append(inv_freq(b, head_size))
+    return np.stack(rows, axis=0)
+
+
+# --------------------------------------------------------------------------- segments
+def segment_ids(seq_lens) -> np.ndarray:
+    """b(t) for every packed token t: tokens are laid out sequence after sequence.
+
+    [DynamicNTKOperation, 算子功能分析]: each batch's positionIds are taken out by its
+    seqLen; positionIds is the concatenation [0..L_0-1, 0..L_1-1, ...] ([输入]).
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    return np.repeat(np.arange(seq_lens.size, dtype=np.int64), seq_lens)
+
+
+def segment_starts(seq_lens) -> np.ndarray:
+    """First packed token index of every sequence (exclusive prefix sum of seqLens)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(seq_lens)[:-1]]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------- a2
+def angles(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32") -> np.ndarray:
+    """freq[t, i] = (pos[t] / s) * f[b(t), i], the outer product per sequence.
+
+    [DynamicNTKOperation, 算子功能分析]: for each batch, freq = einsum('i,j->ij',
+    positionIds, invFreq).  The linear ``rope_scaling_factor`` s of [RoPE-fusion blog,
+    section 5.3] divides positions before the outer product.
+
+    mode "fp32": the division and the product are each rounded to float32, as they
+    are when int32 positions meet float32 inverse frequencies (the parity mode).
+    mode "exact": float64 throughout (used for the relative-position invariant).
+    Returns float64 [T, D/2] holding the (float32-representable in fp32 mode) angles.
+    """
+    pos = np.asarray(pos)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    inv_freq_b = np.asarray(inv_freq_b)
+    if int(seq_lens.sum()) != pos.shape[0]:
+        raise ValueError("sum(seq_lens) must equal ntokens")
+    out = np.empty((pos.shape[0], inv_freq_b.shape[1]), dtype=np.float64)
+    start = 0
+    for b, L in enumerate(seq_lens.tolist()):
+        p = pos[start:start + L]
+        if mode == "fp32":
+            t = p.astype(np.float32) / np.float32(pos_scale)          # fl32(p / s)
+            freq = np.einsum("i,j->ij", t, inv_freq_b[b].astype(np.float32))  # fl32 products
+            out[start:start + L] = freq.astype(np.float64)
+        elif mode == "exact":
+            t = p.astype(np.float64) / float(pos_scale)
+            out[start:start + L] = np.einsum("i,j->ij", t, inv_freq_b[b].astype(np.float64))
+        else:
+            raise ValueError(mode)
+        start += L
+    return out
+
+
+def rope_tables(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32"):
+    """(sin, cos), each float64 [ntokens, D].
+
+    [DynamicNTKOperation, 算子功能分析]: emb = cat((freq, freq), -1); sinOut = emb.sin();
+    cosOut = emb.cos().  Output shape [ntokens, headSize] ([输出]).
+    """
+    freq = angles(pos, inv_freq_b, seq_lens, pos_scale, mode)
+    emb = np.concatenate([freq, freq], axis=-1)
+    return np.sin(emb), np.cos(emb)
+
+
+# --------------------------------------------------------------------------- rotation
+def rotation_matrix(theta_row) -> np.ndarray:
+    """Explicit D x D rotation for one token, from its D/2 angles.
+
+    [RoPE/GQA tutorial, section 六]: the vector is split into 2-D pairs and each pair is
+    rotated by a position-dependent angle; [RoPE-fusion blog, section 一]: each token is
+    multiplied by a position-dependent rotation matrix.  Pairs follow the rotate-half
+    layout of emb = cat(freq, freq): pair i is (x_i, x_{i+D/2}) with angle theta_i.
+    """
+    theta_row = np.asarray(theta_row, dtype=np.float64)
+    half = theta_row.shape[0]
+    D = 2 * half
+    R = np.zeros((D, D), dtype=np.float64)
+    for i in range(half):
+        c, s = np.cos(theta_row[i]), np.sin(theta_row[i])
+        R[i, i] = c
+        R[i, i + half] = -s
+        R[i + half, i] = s
+        R[i + half, i + half] = c
+    return R
+
+
+def rope_op_matrix(cos_row, sin_row) -> np.ndarray:
+    """Explicit D x D matrix of the Rope op for one token, from its table rows.
+
+    [DynamicNTKOperation, 算子上下文]: q, k, sin, cos enter the Rope op, which outputs the
+    rotated q, k.  Written out per element: x'_j = x_j cos_j + rh(x)_j sin_j with
+    rh(x) = cat(-x[D/2:], x[:D/2]).  For tables in the cat(freq, freq) form this is the
+    rotation of ``rotation_matrix``; for arbitrary table values it is the same linear map.
+    """
+    cos_row = np.asarray(cos_row, dtype=np.float64)
+    sin_row = np.asarray(sin_row, dtype=np.float64)
+    D = cos_row.shape[0]
+    half = D // 2
+    M = np.zeros((D, D), dtype=np.float64)
+    for j in range(D):
+        M[j, j] = cos_row[j]
+        if j < half:
+            M[j, j + half] = -sin_row[j]
+        else:
+            M[j, j - half] = sin_row[j]
+    return M
+
+
+def rotate_tokens(x, cos, sin, chunk: int = 512) -> np.ndarray:
+    """Apply each token's explicit Rope-op matrix to x [T, H, D] (float64 out).
+
+    Token t uses rope_op_matrix(cos[t], sin[t]); every head of the token shares it.
+    Matrices are built in token chunks to bound memory.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    T, H, D = x.shape
+    half = D // 2
+    out = np.empty_like(x)
+    idx = np.arange(D)
+    partner = np.where(idx < half, idx + half, idx - half)
+    sign = np.where(idx < half, -1.0, 1.0)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        n = t1 - t0
+        M = np.zeros((n, D, D), dtype=np.float64)
+        M[:, idx, idx] = cos[t0:t1]
+        M[:, idx, partner] = sign[None, :] * sin[t0:t1]
+        out[t0:t1] = np.einsum("tij,thj->thi", M, x[t0:t1])
+    return out
+
+
+# --------------------------------------------------------------------------- attention
+def attention(q, k, v, scale: float, causal: bool = True):
+    """Softmax(Q K^T * scale) V for one head with the full N x N score matrix.
+
+    [FlashAttention blog, "Attention 的显存坑在哪"]: Attention(Q,K,V) = Softmax(QK^T/sqrt(d))V
+    computed in three steps: the (N, N) scores, the row softmax, the product with V.
+    Causal: key j > query i is excluded.  Returns (O [N, D], lse [N]) with
+    lse = log(sum_j exp(score_ij)) over the kept keys.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[0]
+    S = (q @ k.T) * float(scale)
+    if causal:
+        S = np.where(np.tril(np.ones((n, k.shape[0]), dtype=bool)), S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    P = E / l
+    return P @ v, (m[:, 0] + np.log(l[:, 0]))
+
+
+def _check_packed(q, k, v, seq_lens):
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape[0] != T or k.shape[2] != D or v.shape[2] != D:
+        raise ValueError("q, k, v must be packed [T, H, D] with the same T and D")
+    Hkv = k.shape[1]
+    if v.shape[1] != Hkv or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv and k, v must share Hkv")
+    if int(np.sum(seq_lens)) != T:
+        raise ValueError("sum(seq_lens) must equal T")
+    return T, Hq, Hkv, D
+
+
+def rope_attention(q, k, v, cos, sin, seq_lens, scale: float, causal: bool = True):
+    """Full oracle: rotate Q and K with their tokens' tables, then attention per
+    (sequence, q head).  Packed layout: q [T, Hq, D], k/v [T, Hkv, D], tables [T, D].
+
+    GQA ([RoPE/GQA tutorial, section 十二]): q heads are split into Hkv groups of
+    g = Hq / Hkv contiguous heads; group j shares kv head j.
+    Returns (O [T, Hq, D], lse [Hq, T]) in float64.
+    """
+    T, Hq, Hkv, D = _check_packed(q, k, v, seq_lens)
+    g = Hq // Hkv
+    qr = rotate_tokens(q, cos, sin)
+    kr = rotate_tokens(k, cos, sin)
+    v = np.asarray(v, dtype=np.float64)
+    O = np.empty((T, Hq, D), dtype=np.float64)
+    lse = np.empty((Hq, T), dtype=np.float64)
+    for s0, L in zip(segment_starts(seq_lens).tolist(), np.asarray(seq_lens).tolist()):
+        for h in range(Hq):
+            kvh = h // g
+            o, l = attention(qr[s0:s0 + L, h], kr[s0:s0 + L, kvh], v[s0:s0 + L, kvh], scale, causal)
+            O[s0:s0 + L, h] = o
+            lse[h, s0:s0 + L] = l
+    return O, lse
+
+
+def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool, samples):
+    """Oracle output rows O[t, h, :] (and lse) for a list of (t, h) samples only.
+
+    The same definition as ``rope_attention`` evaluated one query row at a time, so
+    that full-size problems can be checked on sampled outputs.  Rotated keys of a
+    (sequence, kv head) are formed once and reused across samples.
+    """
+    T, Hq, Hkv, D = _check_packed(q, k, v, seq_lens)
+    g = Hq // Hkv
+    seg = segment_ids(seq_lens)
+    starts = segment_starts(seq_lens)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    cache = {}
+    outs, lses = [], []
+    for t, h in samples:
+        b = int(seg[t])
+        s0, L = int(starts[b]), int(lens[b])
+        kvh = h // g
+        key = (b, kvh)
+        if key not in cache:
+            kr = rotate_tokens(np.asarray(k[s0:s0 + L, kvh:kvh + 1]), cos[s0:s0 + L], sin[s0:s0 + L])[:, 0]
+            cache[key] = (kr, np.asarray(v[s0:s0 + L, kvh], dtype=np.float64))
+        kr, vv = cache[key]
+        qr = rotate_tokens(np.asarray(q[t:t + 1, h:h + 1]), cos[t:t + 1], sin[t:t + 1])[0, 0]
+        i = t - s0
+        n_keys = i + 1 if causal else L
+        s = (kr[:n_keys] @ qr) * float(scale)
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        outs.append((e / l) @ vv[:n_keys])
+        lses.append(m + np.log(l))
+    return np.stack(outs), np.asarray(lses)
+
+
+# --------------------------------------------------------------------------- numerics helpers
+def round_rne(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest value of a binary format (ties to even),
+    keeping subnormals (no flush).  dtype in {"f16", "bf16", "f32"}; returns float64.
+
+    Used to model the rounding of inputs and tables to their storage type.  Values
+    beyond the format's largest finite number are not expected here (inputs are
+    N(0,1) and tables lie in [-1, 1]).
+    """
+    p, emin = DTYPE_FORMATS[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    mant, exp = np.frexp(x[nz])              # x = mant * 2**exp, 0.5 <= |mant| < 1
+    e = np.maximum(exp - 1, emin)            # exponent of the leading bit, clamped at emin
+    quantum = np.ldexp(1.0, e - (p - 1))     # spacing of representable values there
+    out[nz] = np.rint(x[nz] / quantum) * quantum   # np.rint rounds half to even
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+def ulp(x, dtype: str) -> np.ndarray:
+    """Unit in the last place of the format at |x|: 2^(max(floor(log2|x|), emin) - p + 1).
+
+    At x = 0 this is the smallest subnormal of the format.
+    """
+    p, emin = DTYPE_FORMATS[dtype]
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.full(x.shape, emin, dtype=np.int64)
+    nz = x > 0
+    _, ex = np.frexp(x[nz])
+    e[nz] = np.maximum(ex - 1, emin)
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int64))

@@ -1,0 +1,435 @@
+"""Pins for the CPU oracle: closed forms, invariants, special cases, brute force.
+
+Each check_* function takes the oracle function(s) it checks as arguments, so the
+same check runs against the oracle (must pass) and against planted mistakes
+(must fail; see the mutation tests at the end).  No GPU is used here.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+
+mpmath = pytest.importorskip("mpmath")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------- inv_freq (a1)
+def check_inv_freq(inv_freq):
+    # closed form at small D: 10000^(-0) = 1, 10000^(-2/4) = 0.01
+    f = inv_freq(10000.0, 4)
+    assert f.dtype == np.float32 and f.shape == (2,)
+    assert f[0] == np.float32(1.0) and f[1] == np.float32(0.01)
+    # correctly rounded to float32 against a 40-digit reference, several bases/sizes
+    mpmath.mp.dps = 40
+    for base, D in [(1e4, 64), (1e4, 128), (5e5, 128), (1e6, 128), (1e4, 2048)]:
+        f = inv_freq(base, D)
+        assert f.shape == (D // 2,)
+        for i in range(0, D // 2, max(1, D // 64)):
+            exact = mpmath.power(mpmath.mpf(base), -mpmath.mpf(2 * i) / D)
+            err = abs(mpmath.mpf(float(f[i])) - exact)
+            half_ulp = mpmath.mpf(float(orc.ulp(float(exact), "f32"))) / 2
+            assert err <= half_ulp * (1 + mpmath.mpf("1e-6")), (base, D, i)
+        assert np.all(np.diff(f.astype(np.float64)) < 0)
+
+
+def test_inv_freq_closed_form():
+    check_inv_freq(orc.inv_freq)
+
+
+def test_ntk_base_properties():
+    # Parity unpinned: only the properties the DynamicNTKOperation page states hold.
+    assert orc.ntk_base(1e4, 4096, 4096, 128) == 1e4
+    assert orc.ntk_base(1e4, 512, 4096, 128) == 1e4
+    b = orc.ntk_base(1e4, 8192, 4096, 128)
+    assert b > 1e4
+    assert orc.ntk_base(1e4, 8000, 4096, 128) < b   # enlarges with length
+    f = orc.inv_freq_per_sequence(1e4, [1000, 8192], 128, 4096)
+    assert f.shape == (2, 64) and f.dtype == np.float32
+    assert np.array_equal(f[0], orc.inv_freq(1e4, 128))
+    assert np.all(f[1] <= f[0]) and np.all(f[1] > 0) and np.all(f <= 1)
+
+
+# --------------------------------------------------------------------------- segments and angles
+def test_segment_ids_hand():
+    assert orc.segment_ids([2, 3, 1]).tolist() == [0, 0, 1, 1, 1, 2]
+    assert orc.segment_starts([2, 3, 1]).tolist() == [0, 2, 5]
+
+
+def check_tables_golden(rope_tables, golden):
+    mpmath.mp.dps = 50
+    for case in golden["cases"]:
+        pos = np.array(case["positionIds"], dtype=np.int32)
+        f = np.array(case["invFreq"], dtype=np.float32)
+        s, c = rope_tables(pos, f, case["seqLens"], case["scale"])
+        emb = np.array(case["emb"], dtype=np.float64)
+        for t in range(emb.shape[0]):
+            for j in range(emb.shape[1]):
+                assert abs(s[t, j] - float(mpmath.sin(mpmath.mpf(emb[t, j])))) <= 1e-16, (case["name"], t, j)
+                assert abs(c[t, j] - float(mpmath.cos(mpmath.mpf(emb[t, j])))) <= 1e-16, (case["name"], t, j)
+
+
+def test_tables_golden(golden_dir):
+    with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
+        golden = json.load(fh)
+    check_tables_golden(orc.rope_tables, golden)
+
+
+def check_angles_fp32(angles):
+    r = rng(1)
+    seq_lens = [5, 9, 3]
+    pos = np.concatenate([np.arange(L) for L in seq_lens]).astype(np.int32) * 977
+    f = r.uniform(0.0, 1.0, size=(3, 8)).astype(np.float32)
+    seg = orc.segment_ids(seq_lens)
+    for scale in (1.0, 2.0, 3.0):
+        got = angles(pos, f, seq_lens, scale, "fp32")
+        # independent path: exact float64 quotient/product, each rounded once to float32
+        t = (pos.astype(np.float64) / scale).astype(np.float32).astype(np.float64)
+        want = (t[:, None] * f[seg].astype(np.float64)).astype(np.float32).astype(np.float64)
+        assert np.array_equal(got, want)
+
+
+def test_angles_fp32_rounding():
+    check_angles_fp32(orc.angles)
+
+
+def check_table_structure(rope_tables):
+    r = rng(2)
+    seq_lens = [7, 4]
+    pos = np.concatenate([np.arange(L) for L in seq_lens]).astype(np.int32)
+    f = np.stack([orc.inv_freq(1e4, 64), orc.inv_freq(5e5, 64)])
+    s, c = rope_tables(pos, f, seq_lens, 1.0)
+    assert s.shape == (11, 64) and c.shape == (11, 64)
+    # position 0 of every sequence: cos = 1, sin = 0 exactly
+    for t in (0, 7):
+        assert np.all(c[t] == 1.0) and np.all(s[t] == 0.0)
+    # rotate-half form: column j equals column j + D/2 bit for bit
+    assert np.array_equal(s[:, :32], s[:, 32:]) and np.array_equal(c[:, :32], c[:, 32:])
+    assert np.max(np.abs(s * s + c * c - 1.0)) < 1e-15
+    # each row uses its own sequence's inverse frequencies: t=8 is position 1 of batch 1
+    assert np.allclose(s[8, :32], np.sin(f[1].astype(np.float64)), rtol=0, atol=1e-16)
+    assert np.allclose(s[1, :32], np.sin(f[0].astype(np.float64)), rtol=0, atol=1e-16)
+
+
+def test_table_structure():
+    check_table_structure(orc.rope_tables)
+
+
+# --------------------------------------------------------------------------- rotation
+def check_rotation(rotation_matrix, rope_op_matrix, rotate_tokens):
+    r = rng(3)
+    D = 16
+    theta = r.uniform(-50, 50, size=D // 2)
+    R = rotation_matrix(theta)
+    assert np.array_equal(rotation_matrix(np.zeros(D // 2)), np.eye(D))
+    assert np.max(np.abs(R @ rotation_matrix(-theta) - np.eye(D))) < 1e-14
+    q = r.standard_normal(D)
+    assert abs(np.linalg.norm(R @ q) - np.linalg.norm(q)) <= 1e-12 * np.linalg.norm(q)
+    # pair i is (i, i + D/2) rotated by theta_i: a single-angle check by hand
+    e0 = np.zeros(D)
+    e0[0] = 1.0
+    th = np.zeros(D // 2)
+    th[0] = 0.3
+    got = rotation_matrix(th) @ e0
+    want = np.zeros(D)
+    want[0], want[D // 2] = math.cos(0.3), math.sin(0.3)
+    assert np.max(np.abs(got - want)) < 1e-16
+    # the Rope op on cat(freq, freq) tables is the same rotation
+    emb = np.concatenate([theta, theta])
+    assert np.max(np.abs(rope_op_matrix(np.cos(emb), np.sin(emb)) - R)) < 1e-15
+    # second formulation: x*cos + rotate_half(x)*sin, rotate_half(x) = cat(-x2, x1)
+    x = r.standard_normal((3, 2, D))
+    cos = r.uniform(-1, 1, size=(3, D))
+    sin = r.uniform(-1, 1, size=(3, D))
+    rh = np.concatenate([-x[..., D // 2:], x[..., :D // 2]], axis=-1)
+    want = x * cos[:, None, :] + rh * sin[:, None, :]
+    assert np.max(np.abs(rotate_tokens(x, cos, sin) - want)) < 1e-14
+
+
+def test_rotation():
+    check_rotation(orc.rotation_matrix, orc.rope_op_matrix, orc.rotate_tokens)
+
+
+def check_relative_position(rope_tables, rotate_tokens):
+    # [RoPE/GQA tutorial, section 五]: the rotated score depends only on m - n.
+    r = rng(4)
+    D = 64
+    f = orc.inv_freq(1e4, D)[None, :]
+    q = r.standard_normal((1, 1, D))
+    k = r.standard_normal((1, 1, D))
+    pos = np.arange(0, 1025, dtype=np.int32)
+    s, c = rope_tables(pos, f, [pos.size], 1.0, "exact")
+
+    def score(m, n):
+        qm = rotate_tokens(q, c[m:m + 1], s[m:m + 1])[0, 0]
+        kn = rotate_tokens(k, c[n:n + 1], s[n:n + 1])[0, 0]
+        return qm @ kn
+
+    for m, n, shift in [(5, 2, 100), (300, 17, 700), (0, 0, 1024), (9, 40, 900)]:
+        a, b = score(m, n), score(m + shift, n + shift)
+        assert abs(a - b) <= 1e-12 * max(1.0, abs(a)), (m, n, shift, a, b)
+    # and it does depend on the offset
+    assert abs(score(5, 2) - score(5, 3)) > 1e-3
+
+
+def test_relative_position():
+    check_relative_position(orc.rope_tables, orc.rotate_tokens)
+
+
+# --------------------------------------------------------------------------- attention
+def brute_force_attention(q, k, v, scale, causal):
+    """Scalar loops, independent of the oracle's matrix form."""
+    n, d = len(q), len(q[0])
+    out = []
+    for i in range(n):
+        keys = range(i + 1) if causal else range(len(k))
+        sc = []
+        for j in keys:
+            acc = 0.0
+            for e in range(d):
+                acc += q[i][e] * k[j][e]
+            sc.append(acc * scale)
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        tot = sum(w)
+        row = []
+        for e in range(d):
+            acc = 0.0
+            for jj, j in enumerate(keys):
+                acc += w[jj] * v[j][e]
+            row.append(acc / tot)
+        out.append(row)
+    return np.array(out)
+
+
+def check_attention(attention):
+    r = rng(5)
+    for n, d, causal in [(1, 4, True), (17, 8, True), (64, 16, True), (23, 8, False)]:
+        q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = attention(q, k, v, scale, causal)
+        bf = brute_force_attention(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+        assert np.max(np.abs(o - bf)) < 1e-12, (n, d, causal)
+        # lse = log sum exp of the kept scores (row 0 of a causal problem: one score)
+        if causal:
+            assert abs(lse[0] - (q[0] @ k[0]) * scale) < 1e-12
+    n, d = 40, 8
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    # rows of P sum to 1 (V = ones gives ones), P >= 0 (convex combination bounds)
+    o, _ = attention(q, k, np.ones((n, d)), 0.3, True)
+    assert np.max(np.abs(o - 1.0)) < 1e-14
+    o, _ = attention(q, k, v, 0.3, True)
+    for i in range(n):
+        assert np.all(o[i] <= v[:i + 1].max(axis=0) + 1e-12) and np.all(o[i] >= v[:i + 1].min(axis=0) - 1e-12)
+    # causal row 0 is V[0]; a later key never leaks into an earlier row
+    assert np.max(np.abs(o[0] - v[0])) < 1e-15
+    v2 = v.copy()
+    v2[30:] = 1e6
+    o2, _ = attention(q, k, v2, 0.3, True)
+    assert np.max(np.abs(o2[:30] - o[:30])) < 1e-12
+    # Q = 0: uniform weights over the kept keys -> running mean of V
+    o, _ = attention(np.zeros((n, d)), k, v, 0.7, True)
+    cm = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.max(np.abs(o - cm)) < 1e-13
+    # one dominant logit picks its V row
+    kk = np.zeros((n, d))
+    kk[11, 0] = 1.0
+    qq = np.zeros((n, d))
+    qq[:, 0] = 1e4
+    o, _ = attention(qq, kk, v, 1.0, True)
+    assert np.max(np.abs(o[11:] - v[11])) < 1e-12
+
+
+def test_attention():
+    check_attention(orc.attention)
+
+
+def _packed_problem(r, seq_lens, hq, hkv, d):
+    T = int(np.sum(seq_lens))
+    q = r.standard_normal((T, hq, d))
+    k = r.standard_normal((T, hkv, d))
+    v = r.standard_normal((T, hkv, d))
+    pos = np.concatenate([np.arange(L) for L in seq_lens]).astype(np.int32)
+    f = orc.inv_freq_per_sequence(1e4, seq_lens, d, None)
+    s, c = orc.rope_tables(pos, f, seq_lens, 1.0)
+    return q, k, v, s, c
+
+
+def check_rope_attention(rope_attention, rope_attention_rows):
+    r = rng(6)
+    d = 16
+    scale = 1.0 / math.sqrt(d)
+    # GQA reduces to MHA with each kv head repeated g times (contiguous groups)
+    seq_lens = [19]
+    q, k, v, s, c = _packed_problem(r, seq_lens, 8, 2, d)
+    o_gqa, lse_gqa = rope_attention(q, k, v, c, s, seq_lens, scale, True)
+    o_mha, lse_mha = rope_attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), c, s, seq_lens, scale, True)
+    assert np.max(np.abs(o_gqa - o_mha)) < 1e-14 and np.max(np.abs(lse_gqa - lse_mha)) < 1e-14
+    # varlen: packed output = each sequence run on its own
+    seq_lens = [5, 12, 1, 9]
+    q, k, v, s, c = _packed_problem(r, seq_lens, 4, 2, d)
+    o, lse = rope_attention(q, k, v, c, s, seq_lens, scale, True)
+    for s0, L in zip(orc.segment_starts(seq_lens), seq_lens):
+        sl = slice(s0, s0 + L)
+        oi, li = rope_attention(q[sl], k[sl], v[sl], c[sl], s[sl], [L], scale, True)
+        assert np.max(np.abs(o[sl] - oi)) < 1e-14 and np.max(np.abs(lse[:, sl] - li)) < 1e-14
+    # segment probe: Q = 0, V column 0 = segment id -> output column 0 = segment id
+    vv = v.copy()
+    vv[:, :, 0] = orc.segment_ids(seq_lens)[:, None]
+    o0, _ = rope_attention(np.zeros_like(q), k, vv, c, s, seq_lens, scale, True)
+    assert np.max(np.abs(o0[:, :, 0] - orc.segment_ids(seq_lens)[:, None])) < 1e-14
+    # zero angles reduce to plain attention on the unrotated inputs
+    z = np.zeros_like(s)
+    o_z, _ = rope_attention(q, k, v, np.ones_like(c), z, seq_lens, scale, True)
+    s0, L = 5, 12
+    o_p, _ = orc.attention(q[s0:s0 + L, 3], k[s0:s0 + L, 1], v[s0:s0 + L, 1], scale, True)
+    assert np.max(np.abs(o_z[s0:s0 + L, 3] - o_p)) < 1e-14
+    # sampled rows equal the full result
+    samples = [(0, 0), (4, 3), (5, 1), (16, 2), (17, 0), (26, 3)]
+    rows, lses = rope_attention_rows(q, k, v, c, s, seq_lens, scale, True, samples)
+    for (t, h), row, l in zip(samples, rows, lses):
+        assert np.max(np.abs(row - o[t, h])) < 1e-13 and abs(l - lse[h, t]) < 1e-13
+
+
+def test_rope_attention():
+    check_rope_attention(orc.rope_attention, orc.rope_attention_rows)
+
+
+# --------------------------------------------------------------------------- rounding helpers
+def test_round_rne_matches_library_casts():
+    r = rng(7)
+    x32 = np.concatenate([
+        r.standard_normal(20000).astype(np.float32),
+        (r.standard_normal(4000) * 1e-38).astype(np.float32),        # bf16 subnormal range
+        np.array([1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 2**-130, 0.0], dtype=np.float32),  # ties
+    ])
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.round_rne(x32.astype(np.float64), "bf16"), want)
+    x64 = np.concatenate([r.standard_normal(20000), r.standard_normal(4000) * 1e-5,
+                          np.array([1 + 2**-11, 1 + 3 * 2**-11, 2**-25, 3 * 2**-25, 0.0])])
+    assert np.array_equal(orc.round_rne(x64, "f16"), x64.astype(np.float16).astype(np.float64))
+    assert np.array_equal(orc.round_rne(x64, "f32"), x64.astype(np.float32).astype(np.float64))
+
+
+def test_ulp_values():
+    assert orc.ulp(1.0, "bf16") == 2**-7
+    assert orc.ulp(1.0, "f16") == 2**-10
+    assert orc.ulp(1.5, "f32") == 2**-23
+    assert orc.ulp(0.0, "f16") == 2**-24
+    assert orc.ulp(5.8e-5, "f16") == 2**-24      # subnormal range of fp16
+    assert orc.ulp(-0.75, "bf16") == 2**-8
+
+
+# --------------------------------------------------------------------------- planted mistakes
+# Each mutant is one plausible slip; at least one pin above must reject it.
+
+def _mut_inv_freq_off_by_one(base, D):
+    exps = np.arange(1, D + 1, 2, dtype=np.float64) / float(D)
+    return (1.0 / (float(base) ** exps)).astype(np.float32)
+
+
+def _mut_tables_no_concat(pos, f, seq_lens, scale=1.0, mode="fp32"):
+    freq = orc.angles(pos, f, seq_lens, scale, mode)
+    emb = np.repeat(freq, 2, axis=-1)      # interleaved instead of cat(freq, freq)
+    return np.sin(emb), np.cos(emb)
+
+
+def _mut_tables_wrong_batch(pos, f, seq_lens, scale=1.0, mode="fp32"):
+    # every token uses batch 0's inverse frequencies
+    f0 = np.repeat(np.asarray(f)[:1], len(seq_lens), axis=0)
+    return orc.rope_tables(pos, f0, seq_lens, scale, mode)
+
+
+def _mut_tables_scale_times(pos, f, seq_lens, scale=1.0, mode="fp32"):
+    return orc.rope_tables(pos, f, seq_lens, 1.0 / scale, mode)
+
+
+def _mut_angles_fp64(pos, f, seq_lens, scale=1.0, mode="fp32"):
+    return orc.angles(pos, f, seq_lens, scale, "exact")
+
+
+def _mut_rotation_adjacent(theta):
+    D = 2 * len(theta)
+    R = np.zeros((D, D))
+    for i, th in enumerate(theta):
+        c, s = math.cos(th), math.sin(th)
+        R[2 * i, 2 * i], R[2 * i, 2 * i + 1], R[2 * i + 1, 2 * i], R[2 * i + 1, 2 * i + 1] = c, -s, s, c
+    return R
+
+
+def _mut_rotate_tokens_sign(x, cos, sin, chunk=512):
+    return orc.rotate_tokens(x, cos, -np.asarray(sin))
+
+
+def _mut_rotate_tokens_no_cos(x, cos, sin, chunk=512):
+    return orc.rotate_tokens(x, np.ones_like(cos), sin)
+
+
+def _mut_attention_no_scale(q, k, v, scale, causal=True):
+    return orc.attention(q, k, v, 1.0, causal)
+
+
+def _mut_attention_mask_offset(q, k, v, scale, causal=True):
+    q = np.asarray(q, dtype=np.float64)
+    n = q.shape[0]
+    S = (q @ np.asarray(k).T) * scale
+    if causal:
+        S = np.where(np.tril(np.ones((n, n), dtype=bool), -1) | (n == 1), S, -np.inf)
+        S[0, 0] = (q[0] @ np.asarray(k)[0]) * scale
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ np.asarray(v), m[:, 0] + np.log(l[:, 0])
+
+
+def _mut_attention_transposed(q, k, v, scale, causal=True):
+    o, lse = orc.attention(q, k, v, scale, causal)
+    P = np.asarray(q) @ np.asarray(k).T * scale
+    n = P.shape[0]
+    if causal:
+        P = np.where(np.tril(np.ones((n, n), dtype=bool)), P, -np.inf)
+    P = np.exp(P - P.max(axis=0, keepdims=True))   # normalised over the wrong axis
+    P = P / P.sum(axis=0, keepdims=True)
+    return P @ np.asarray(v), lse
+
+
+def _mut_rope_attention_gqa_strided(q, k, v, cos, sin, seq_lens, scale, causal=True):
+    hq, hkv = q.shape[1], k.shape[1]
+    idx = np.arange(hq) % hkv                      # strided instead of contiguous groups
+    return orc.rope_attention(q, np.asarray(k)[:, idx], np.asarray(v)[:, idx], cos, sin, seq_lens, scale, causal)
+
+
+def _mut_rope_attention_no_segments(q, k, v, cos, sin, seq_lens, scale, causal=True):
+    return orc.rope_attention(q, k, v, cos, sin, [int(np.sum(seq_lens))], scale, causal)
+
+
+@pytest.mark.parametrize("name,run", [
+    ("inv_freq off by one", lambda g: check_inv_freq(_mut_inv_freq_off_by_one)),
+    ("tables interleaved", lambda g: check_table_structure(_mut_tables_no_concat)),
+    ("tables interleaved (golden)", lambda g: check_tables_golden(_mut_tables_no_concat, g)),
+    ("tables wrong batch row", lambda g: check_tables_golden(_mut_tables_wrong_batch, g)),
+    ("scaling multiplies", lambda g: check_tables_golden(_mut_tables_scale_times, g)),
+    ("angles not rounded to fp32", lambda g: check_angles_fp32(_mut_angles_fp64)),
+    ("adjacent pairs", lambda g: check_rotation(_mut_rotation_adjacent, orc.rope_op_matrix, orc.rotate_tokens)),
+    ("rotation sign", lambda g: check_rotation(orc.rotation_matrix, orc.rope_op_matrix, _mut_rotate_tokens_sign)),
+    ("rotation drops cos", lambda g: check_rotation(orc.rotation_matrix, orc.rope_op_matrix, _mut_rotate_tokens_no_cos)),
+    ("relative position, no cos", lambda g: check_relative_position(orc.rope_tables, _mut_rotate_tokens_no_cos)),
+    ("attention drops scale", lambda g: check_attention(_mut_attention_no_scale)),
+    ("causal mask off by one", lambda g: check_attention(_mut_attention_mask_offset)),
+    ("softmax over wrong axis", lambda g: check_attention(_mut_attention_transposed)),
+    ("GQA strided groups", lambda g: check_rope_attention(_mut_rope_attention_gqa_strided, orc.rope_attention_rows)),
+    ("segments ignored", lambda g: check_rope_attention(_mut_rope_attention_no_segments, orc.rope_attention_rows)),
+])
+def test_pins_reject_planted_mistakes(name, run, golden_dir):
+    with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
+        golden = json.load(fh)
+    with pytest.raises(AssertionError):
+        run(golden)
