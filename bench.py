@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RoPE + FlashAttention forward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic inputs already resident in HBM:
+rope_tables (cos/sin for positions 0..S-1) followed by rope_flash_attn_fwd (rotation of
+Q/K in registers, causal attention).  The host inverse frequencies are computed once at
+set-up (a model-load-time quantity).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+The value is TFLOP/s of causal attention (4*B*Hq*S^2*D/2 per step) over the timed
+steps.  The roofline object reports the attention kernel's own time, measured with HIP
+events on the stream it runs on, against the dense bf16 MFMA peak.  Extra measurements
+(after the timed region): rope_tables GB/s at the op's size limits, rope_qk GB/s on the
+workload, and the unfused path (rope_qk + attention without rotation) for the fusion
+ablation.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused RoPE+FlashAttn fwd TFLOP/s and % bf16 MFMA peak; rope_tables GB/s"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA peaks (f32: matrix fp32)
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.hip", "rope_flashattention_amd/csrc/common.h"]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_key):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_flash_fwd_{workload_key}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(KERNEL_SOURCES):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def time_events(fn, reps, torch):
+    """Median device time (ms) of fn over reps launches, HIP events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return median([a.elapsed_time(b) for a, b in evs])
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle as it stands on sequence 0, one q head at a time, until the budget is spent."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    w = inp.workload
+    S = int(inp.seq_lens[0])
+    q, k, v = inp.packed()
+    q, k, v = q[:S], k[:S], v[:S]
+    g = w.hq // w.hkv
+    t0 = time.perf_counter()
+    f = orc.inv_freq_per_sequence(w.base, inp.seq_lens[:1], w.head_dim, w.trained_len)
+    s, c = orc.rope_tables(inp.pos[:S], f, inp.seq_lens[:1], w.pos_scale)
+    s, c = orc.round_rne(s, w.dtype), orc.round_rne(c, w.dtype)
+    heads = 0
+    while heads < w.hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        h = heads
+        orc.rope_attention(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1], c, s, [S],
+                           w.softmax_scale, w.causal)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = 4.0 * heads * S * S * w.head_dim / (2.0 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0 (S={S}), {heads} of {w.hq} q heads, full causal rows, tables included; "
+                      f"{dt:.1f} s wall, numpy float64 with {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: the S=2048 MHA workload)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the table/rope_qk/unfused measurements")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import rope_flashattention_amd as rfa
+    from rope_flashattention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rfa.lib()
+    dev = torch.device("cuda:0")
+    w = wl.CONFIGS[args.config]
+    inp = wl.generate(w)
+    D = w.head_dim
+
+    # ---- set-up: inputs resident in HBM, host inverse frequencies, output buffers
+    if w.varlen:
+        q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+        f = torch.from_numpy(rfa.inv_freq(w.base, D, inp.seq_lens, w.trained_len)).to(dev)
+        pos = torch.from_numpy(inp.pos).to(dev)
+        tab_lens = inp.seq_lens
+        cu = torch.from_numpy(wl.cu_seqlens(inp.seq_lens)).to(dev)
+        akw = dict(layout="TND", cu_seqlens=cu, max_seqlen=int(inp.seq_lens.max()))
+    else:
+        q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+        f = torch.from_numpy(rfa.inv_freq(w.base, D, [w.seqlen], w.trained_len)).to(dev)
+        pos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)   # one table shared by the batch
+        tab_lens = np.array([w.seqlen], dtype=np.int32)
+        akw = dict(layout="BNSD")
+    T_tab = int(tab_lens.sum())
+    sin = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
+    cos = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        rfa.rope_tables(pos, f, tab_lens, D, w.pos_scale, w.torch_dtype, sin, cos)
+        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps; attention launches bracketed by events on their stream
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        rfa.rope_tables(pos, f, tab_lens, D, w.pos_scale, w.torch_dtype, sin, cos)
+        ev[i][1].record()
+        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    flops = wl.causal_flops(w, inp.seq_lens)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    att_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    tab_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    wkey = f"cfg{args.config}"
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to the dtype, positions 0..L-1 per sequence",
+        "config": {"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": D,
+                   "seq_len": (int(inp.seq_lens.max()) if w.varlen else w.seqlen),
+                   "ntokens": inp.ntokens, "causal": w.causal, "rope_base": w.base,
+                   "ntk_trained_len": w.trained_len, "pos_scale": w.pos_scale, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": read_traffic(wkey),
+                     "kernel": "flash_fwd_kernel", "avg_launch_ms": round(att_ms, 4)},
+        "components": {"rope_tables_ms": round(tab_ms, 5), "attention_ms": round(att_ms, 4),
+                       "attention_tflops": round(achieved, 2)},
+    }
+
+    if not args.no_extras:
+        comp = result["components"]
+        # rope_qk on the workload (reads Q, K; writes Q', K'; table rows read once)
+        if w.varlen:
+            qkw = dict(layout="TND", cu_seqlens=akw["cu_seqlens"], max_seqlen=akw["max_seqlen"])
+            sq, cq = sin, cos
+            tsr = 0
+        else:
+            qkw = dict(layout="BNSD")
+            sq, cq, tsr = sin, cos, 0
+        oq, ok = torch.empty_like(q), torch.empty_like(k)
+        ms = time_events(lambda: rfa.rope_qk(q, k, cq, sq, table_seq_rows=tsr, out_q=oq, out_k=ok, **qkw), 20, torch)
+        qk_bytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * sq.numel() * sq.element_size()
+        comp["rope_qk_ms"] = round(ms, 4)
+        comp["rope_qk_gbps"] = round(qk_bytes / (ms * 1e-3) / 1e9, 1)
+        comp["rope_qk_hbm_frac"] = round(qk_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        # fusion ablation: unfused = rope_qk + attention on the rotated tensors
+        ms_plain = time_events(lambda: rfa.rope_flash_attn_fwd(oq, ok, v, None, None, causal=w.causal,
+                                                               softmax_scale=w.softmax_scale, out=out, **akw), 10, torch)
+        comp["unfused_ms"] = round(ms + ms_plain, 4)
+        comp["fused_ms"] = round(att_ms, 4)
+        del oq, ok
+        # rope_tables at the op's limits: batch 16, ntokens 256000, head_size 2048 (2.1 GB written)
+        lens = np.full(16, 16000, dtype=np.int32)
+        tpos = torch.arange(16000, dtype=torch.int32, device=dev).repeat(16)
+        for dt_name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+            tf = torch.from_numpy(rfa.inv_freq(1e4, 2048, lens, 4096)).to(dev)
+            ts = torch.empty((256000, 2048), dtype=dt, device=dev)
+            tc = torch.empty((256000, 2048), dtype=dt, device=dev)
+            ms = time_events(lambda: rfa.rope_tables(tpos, tf, lens, 2048, 1.0, dt, ts, tc), 10, torch)
+            tb = 2 * 256000 * 2048 * 2 + 4 * 256000 + 4 * 16 * 1024
+            comp[f"rope_tables_{dt_name}_T256000_D2048_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
+            comp[f"rope_tables_{dt_name}_T256000_D2048_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del ts, tc
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * rope_fa.h — C ABI of librope_fa.so: rotary position embedding (RoPE) tables,
+ * the standalone rotate-half RoPE of Q and K, and RoPE fused into a causal
+ * FlashAttention-style forward pass, for AMD Instinct MI355X (gfx950).
+ *
+ * Page key for the citations below (the source pages of the method):
+ *   [RoPE-fusion blog]     devpress.csdn.net/awstech/6a91ac403bda720d4b352e13
+ *   [FlashAttention blog]  hwcomputing.csdn.net/6a0d3f5c662f9a54cb75d0b0
+ *   [DynamicNTKOperation]  hiascend.com API page ascendtb_01_0140
+ *   [RoPE/GQA tutorial]    smarter.xin/posts/3494b8a4
+ *
+ * Conventions shared by every entry point:
+ *  - Plain C types only; no exception crosses this boundary.
+ *  - The caller owns every buffer.  The library allocates no device or host
+ *    memory and keeps no mutable global state; entry points are re-entrant.
+ *  - Device work is enqueued on the caller's HIP stream (`hip_stream`, a
+ *    hipStream_t passed as void*, NULL = the default stream) and is
+ *    asynchronous: nothing here synchronizes the device.
+ *  - Every argument is validated on the host before any HIP call.  On any
+ *    error the call returns a non-zero rope_status, enqueues nothing and
+ *    writes nothing.  An argument the kernels cannot serve (a head_dim, a
+ *    stride, an alignment) is an error, never a silent fallback to another
+ *    path (the [RoPE-fusion blog] and its sibling pages warn that fused
+ *    operators silently falling back is the failure mode to avoid).
+ *  - Device pointers must be 16-byte aligned and every row stride a multiple
+ *    of 16 bytes (vectorized 16-byte accesses); otherwise ROPE_ERR_UNSUPPORTED.
+ */
+#ifndef ROPE_FA_H
+#define ROPE_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROPE_FA_ABI_VERSION 1
+
+typedef enum rope_status {
+    ROPE_OK = 0,
+    ROPE_ERR_NULL = 1,         /* a required pointer is NULL */
+    ROPE_ERR_SHAPE = 2,        /* non-positive or inconsistent sizes */
+    ROPE_ERR_DTYPE = 3,        /* dtype UNDEFINED, unknown, or not allowed for this argument */
+    ROPE_ERR_LIMIT = 4,        /* a documented size limit is exceeded */
+    ROPE_ERR_UNSUPPORTED = 5,  /* well-formed but not served by the kernels (head_dim, stride, alignment) */
+    ROPE_ERR_ABI = 6,          /* struct_size mismatch or reserved bytes not zero */
+    ROPE_ERR_HIP = 7           /* the HIP runtime reported an error for a launch */
+} rope_status;
+
+/* Element types.  UNDEFINED is never valid ([DynamicNTKOperation], 参数列表:
+ * outDataType defaults to an unusable UNDEFINED that the caller must replace). */
+typedef enum rope_dtype {
+    ROPE_DT_UNDEFINED = 0,
+    ROPE_DT_F16 = 1,
+    ROPE_DT_BF16 = 2,
+    ROPE_DT_F32 = 3
+} rope_dtype;
+
+/* Limits of the table op ([DynamicNTKOperation], 约束说明). */
+#define ROPE_MAX_HEAD_SIZE 2048   /* head_size <= 2048 and a multiple of 32 */
+#define ROPE_MAX_BATCH 16         /* batch <= 16 */
+#define ROPE_MAX_NTOKENS 256000   /* ntokens <= 256000 */
+
+/*
+ * rope_inv_freq — host-side inverse frequencies, one row per sequence.
+ *
+ * out[b, i] = fl32(1 / base_b ** (2i / head_size)), i < head_size/2
+ * ([RoPE-fusion blog], section 1.2 snippet: freqs = 1/(base**(arange(0,D,2)/D))),
+ * formed in double precision and rounded once to float.
+ * base_b = base when trained_len <= 0 or seq_lens[b] <= trained_len; otherwise the
+ * dynamic-NTK enlarged base base * (seq_lens[b] / trained_len) ** (D / (D - 2))
+ * ([DynamicNTKOperation], 功能说明: no interpolation up to the trained length, base
+ * enlarged above it; the page's own enlargement formula is lost, this law is the
+ * reading taken).
+ *
+ *   base       > 0 and finite.
+ *   head_size  even, 2..ROPE_MAX_HEAD_SIZE.
+ *   seq_lens   HOST [batch] int32, each > 0; may be NULL only when trained_len <= 0.
+ *   batch      1..ROPE_MAX_BATCH.
+ *   out        HOST [batch, head_size/2] float, row-major, written by the call.
+ * Pure host computation; no HIP call.  Errors: NULL, SHAPE, LIMIT.
+ */
+rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_lens, int32_t batch,
+                          int32_t trained_len, float* out);
+
+/*
+ * rope_tables — the cos/sin tables of the DynamicNTK op ([DynamicNTKOperation],
+ * 算子功能分析): for each sequence b and each of its tokens t,
+ *   freq[t, i] = fl32(fl32(pos[t] / pos_scale) * inv_freq[b, i]),   i < head_size/2
+ *   emb = cat(freq, freq);  sin_out[t, :] = sin(emb);  cos_out[t, :] = cos(emb)
+ * rounded to nearest-even into out_dtype (fp16 subnormals kept).  pos_scale is the
+ * linear rope_scaling_factor of the [RoPE-fusion blog], section 5.3 (positions are
+ * divided by it before the outer product; 1.0f = no scaling).
+ *
+ *   pos        DEVICE [ntokens] int32, packed sequence after sequence ([DynamicNTKOperation],
+ *              输入: positionIds restart at 0 for each batch; any int32 value is accepted).
+ *   inv_freq   DEVICE [batch, head_size/2] float, row-major (row b serves sequence b).
+ *   seq_lens   HOST [batch] int32, each > 0, sum == ntokens.
+ *   batch      1..ROPE_MAX_BATCH;  ntokens 1..ROPE_MAX_NTOKENS;
+ *   head_size  multiple of 32, 32..ROPE_MAX_HEAD_SIZE.
+ *   pos_scale  finite and > 0.
+ *   out_dtype  ROPE_DT_F16 or ROPE_DT_BF16 (the page's two choices) or ROPE_DT_F32
+ *              (an extension for float32 attention); UNDEFINED -> ROPE_ERR_DTYPE.
+ *   sin_out, cos_out  DEVICE [ntokens, head_size] of out_dtype, row-major, contiguous.
+ * Errors: NULL, SHAPE (sum(seq_lens) != ntokens, seq_len <= 0), LIMIT, DTYPE,
+ * UNSUPPORTED (alignment), HIP.  One kernel launch.
+ */
+rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens,
+                        int32_t batch, int32_t ntokens, int32_t head_size, float pos_scale,
+                        rope_dtype out_dtype, void* sin_out, void* cos_out, void* hip_stream);
+
+/*
+ * Parameters of rope_qk and rope_flash_attn_fwd.
+ *
+ * Q has hq heads, K and V have hkv heads; hq % hkv == 0 and q head h reads kv head
+ * h / (hq / hkv) (contiguous groups; [RoPE/GQA tutorial], sections 十一-十二: query
+ * heads split into groups, each group sharing one K/V head).
+ *
+ * Token addressing.  Dense batches (cu_seqlens == NULL): sequence b, token s < seqlen of
+ * head h lives at base + b*stride[0] + s*stride[1] + h*stride[2] + d*stride[3].  This
+ * covers BNSD ([B, H, S, D], the input_layout of the [RoPE-fusion blog], section 三) and
+ * BSND.  Packed varlen batches (cu_seqlens != NULL): token s of sequence b is packed row
+ * t = cu_seqlens[b] + s at base + t*stride[1] + h*stride[2] + d*stride[3]; stride[0] is
+ * ignored.  stride[3] (the head_dim stride) must be 1.  Strides are in elements.
+ *
+ * Tables (cos, sin) are [rows, head_dim] of table_dtype, row-major and contiguous, as
+ * rope_tables writes them.  Row of token (b, s):
+ *   varlen: the packed row cu_seqlens[b] + s;
+ *   dense:  s when table_seq_rows == 0 (one table shared by every sequence), else
+ *           b * table_seq_rows + s (table_seq_rows >= seqlen).
+ * cos == sin == NULL disables the rotation (plain attention; rope_flash_attn_fwd only).
+ */
+typedef struct rope_attn_params {
+    uint32_t struct_size;       /* = sizeof(rope_attn_params), else ROPE_ERR_ABI */
+    rope_dtype dtype;           /* q, k, v, out, out_q, out_k: F32 | F16 | BF16 */
+    const void* q;              /* DEVICE, hq heads */
+    const void* k;              /* DEVICE, hkv heads */
+    const void* v;              /* DEVICE, hkv heads (rope_flash_attn_fwd only) */
+    void* out;                  /* DEVICE, hq heads, layout by o_stride (rope_flash_attn_fwd) */
+    void* out_q;                /* DEVICE, rope_qk only: rotated q, strides q_stride; may equal q */
+    void* out_k;                /* DEVICE, rope_qk only: rotated k, strides k_stride; may equal k */
+    float* lse;                 /* DEVICE float [hq, ntokens] or NULL: natural-log sum of exp of the
+                                   scaled scores per query row (token index as for tables, varlen:
+                                   packed row, dense: b*seqlen + s) */
+    int32_t batch;              /* number of sequences, >= 1 */
+    int32_t hq, hkv;            /* heads of q and of k/v */
+    int32_t head_dim;           /* rope_qk: multiple of 32, <= 2048; attention: 64 or 128 */
+    int32_t seqlen;             /* dense: tokens per sequence; varlen: ignored (set 0) */
+    int32_t max_seqlen;         /* varlen: HOST upper bound of every sequence length */
+    int32_t ntokens;            /* varlen: HOST total tokens = cu_seqlens[batch]; dense: 0 or batch*seqlen */
+    int32_t causal;             /* 0 or 1 (rope_flash_attn_fwd) */
+    const int32_t* cu_seqlens;  /* DEVICE [batch + 1] int32 prefix sums starting at 0, or NULL = dense */
+    int64_t q_stride[4];        /* {batch, token, head, dim} in elements */
+    int64_t k_stride[4];
+    int64_t v_stride[4];
+    int64_t o_stride[4];
+    const void* cos;            /* DEVICE [rows, head_dim] of table_dtype, or NULL (with sin) */
+    const void* sin;
+    rope_dtype table_dtype;     /* must equal dtype when tables are given */
+    int32_t table_seq_rows;     /* dense only, see above */
+    float softmax_scale;        /* multiplies q.k before the softmax; the caller passes 1/sqrt(head_dim)
+                                   ([FlashAttention blog]: Softmax(QK^T/sqrt(d))V) */
+    uint8_t rsv[16];            /* reserved, must be zero (cf. the rsv[] of DynamicNTKParam) */
+} rope_attn_params;
+
+/*
+ * rope_qk — standalone RoPE of Q and K: the Rope op that consumes the DynamicNTK
+ * tables ([DynamicNTKOperation], 算子上下文: q, k, sin, cos in, rotated q, k out),
+ * the unfused "RoPE, write to HBM, then attention" step of the [RoPE-fusion blog],
+ * section 二.  For every token and head of q and of k, with x a head row of length
+ * D = head_dim and the token's table rows cos, sin:
+ *   x'[j] = x[j]*cos[j] + rotate_half(x)[j]*sin[j],  rotate_half(x) = cat(-x[D/2:], x[:D/2])
+ * computed in float32 and rounded to nearest-even into dtype.  All D table columns are
+ * read.  Uses q, k, out_q, out_k, cos, sin, table_dtype, table_seq_rows, batch, hq, hkv,
+ * head_dim, seqlen / cu_seqlens / ntokens, q_stride (also for out_q), k_stride (also for
+ * out_k).  In-place (out_q == q, out_k == k) is allowed; other overlap is not.
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
+ */
+rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
+
+/*
+ * rope_flash_attn_fwd — RoPE fused into a FlashAttention forward pass
+ * ([RoPE-fusion blog], section 三: one fused operator so rotated Q/K never return to
+ * HBM; [FlashAttention blog]: tiled QK^T, online softmax with a running row max and
+ * row sum, then PV).  For every sequence b, q head h and query s of that sequence:
+ *   q' = rope(q[b, s, h]),  k'_j = rope(k[b, j, h / g])   (the rope_qk formula)
+ *   out[b, s, h] = sum_j softmax_j(softmax_scale * q'.k'_j) v[b, j, h / g]
+ * over keys j <= s when causal (within the sequence), else all j < length.
+ * The kernel reads only table columns [0, head_dim/2) and applies them to both halves:
+ * tables must be in the cat(freq, freq) form that rope_tables produces (unchecked).
+ * Supported: head_dim 64 or 128 with F16, BF16 (fp16/bf16 matrix cores with float32
+ * accumulation); head_dim 64 with F32 (float32 matrix cores).  Optional lse output (see above).
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
+ */
+rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream);
+
+/* Static text for a status code ("ROPE_OK", ...); never NULL. */
+const char* rope_status_str(rope_status s);
+
+/* ROPE_FA_ABI_VERSION of the loaded library. */
+int32_t rope_abi_version(void);
+
+/* sizeof(rope_attn_params) as compiled into the library (for bindings to check). */
+uint32_t rope_attn_params_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_FA_H */

@@ -1,0 +1,283 @@
+"""Python binding of librope_fa.so: fused RoPE + FlashAttention forward on MI355X.
+
+The functions here only marshal torch tensors into the C ABI of ``include/rope_fa.h``
+(pointers, sizes, strides, the current HIP stream); every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library is missing or a
+call is rejected, an exception is raised.
+
+Names follow the C ABI: ``inv_freq`` (rope_inv_freq), ``rope_tables``, ``rope_qk``,
+``rope_flash_attn_fwd``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "RopeError",
+    "lib",
+    "inv_freq",
+    "rope_tables",
+    "rope_qk",
+    "rope_flash_attn_fwd",
+    "RopeAttnParams",
+    "STATUS",
+    "DTYPE",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_fa.so")
+
+STATUS = {0: "ROPE_OK", 1: "ROPE_ERR_NULL", 2: "ROPE_ERR_SHAPE", 3: "ROPE_ERR_DTYPE", 4: "ROPE_ERR_LIMIT",
+          5: "ROPE_ERR_UNSUPPORTED", 6: "ROPE_ERR_ABI", 7: "ROPE_ERR_HIP"}
+DTYPE = {None: 0, torch.float16: 1, torch.bfloat16: 2, torch.float32: 3}
+ABI_VERSION = 1
+
+
+class RopeError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{func} failed: {self.name}")
+
+
+class RopeAttnParams(ctypes.Structure):
+    """Mirror of ``rope_attn_params`` in include/rope_fa.h (checked against the library's size)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("out_q", ctypes.c_void_p),
+        ("out_k", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("ntokens", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 4),
+        ("k_stride", ctypes.c_int64 * 4),
+        ("v_stride", ctypes.c_int64 * 4),
+        ("o_stride", ctypes.c_int64 * 4),
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("table_dtype", ctypes.c_int),
+        ("table_seq_rows", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("rsv", ctypes.c_uint8 * 16),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librope_fa.so once, declare the prototypes, check the ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built (python -m rope_flashattention_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+    L.rope_inv_freq.argtypes = [ctypes.c_double, i32, vp, i32, i32, vp]
+    L.rope_inv_freq.restype = st
+    L.rope_tables.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, ctypes.c_int, vp, vp, vp]
+    L.rope_tables.restype = st
+    L.rope_qk.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
+    L.rope_qk.restype = st
+    L.rope_flash_attn_fwd.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
+    L.rope_flash_attn_fwd.restype = st
+    L.rope_status_str.argtypes = [ctypes.c_int]
+    L.rope_status_str.restype = ctypes.c_char_p
+    L.rope_abi_version.restype = i32
+    L.rope_attn_params_size.restype = ctypes.c_uint32
+    if L.rope_abi_version() != ABI_VERSION:
+        raise RuntimeError("librope_fa ABI version mismatch")
+    if L.rope_attn_params_size() != ctypes.sizeof(RopeAttnParams):
+        raise RuntimeError("rope_attn_params layout mismatch between binding and library")
+    _lib = L
+    return L
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        raise RopeError(func, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _i32_host(seq_lens: Sequence[int]) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+
+
+# --------------------------------------------------------------------------- rope_inv_freq
+def inv_freq(base: float, head_size: int, seq_lens: Optional[Sequence[int]] = None,
+             trained_len: Optional[int] = None, batch: int = 1) -> np.ndarray:
+    """Host inverse frequencies [batch, head_size/2] float32 (rope_inv_freq)."""
+    sl = None if seq_lens is None else _i32_host(seq_lens)
+    nb = batch if sl is None else int(sl.size)
+    out = np.empty((nb, head_size // 2), dtype=np.float32)
+    st = lib().rope_inv_freq(float(base), int(head_size), None if sl is None else sl.ctypes.data, nb,
+                             int(trained_len or 0), out.ctypes.data)
+    _check("rope_inv_freq", st)
+    return out
+
+
+# --------------------------------------------------------------------------- rope_tables
+def rope_tables(pos: torch.Tensor, inv_freq_dev: torch.Tensor, seq_lens: Sequence[int], head_size: int,
+                pos_scale: float = 1.0, out_dtype=torch.bfloat16, sin_out: Optional[torch.Tensor] = None,
+                cos_out: Optional[torch.Tensor] = None):
+    """(sin, cos) tables [ntokens, head_size] on the GPU (rope_tables)."""
+    _need_cuda(pos, inv_freq_dev, sin_out, cos_out)
+    if pos.dtype != torch.int32 or inv_freq_dev.dtype != torch.float32:
+        raise ValueError("pos must be int32 and inv_freq float32")
+    if not (pos.is_contiguous() and inv_freq_dev.is_contiguous()):
+        raise ValueError("pos and inv_freq must be contiguous")
+    sl = _i32_host(seq_lens)
+    n = pos.numel()
+    if inv_freq_dev.numel() != sl.size * (head_size // 2):
+        raise ValueError("inv_freq must be [batch, head_size/2]")
+    if sin_out is None:
+        sin_out = torch.empty((n, head_size), dtype=out_dtype, device=pos.device)
+    if cos_out is None:
+        cos_out = torch.empty((n, head_size), dtype=out_dtype, device=pos.device)
+    for t in (sin_out, cos_out):
+        if t.shape != (n, head_size) or not t.is_contiguous() or t.dtype != out_dtype:
+            raise ValueError("sin_out/cos_out must be contiguous [ntokens, head_size] of out_dtype")
+    st = lib().rope_tables(pos.data_ptr(), inv_freq_dev.data_ptr(), sl.ctypes.data, int(sl.size), n, int(head_size),
+                           float(pos_scale), DTYPE.get(out_dtype, -1), sin_out.data_ptr(), cos_out.data_ptr(),
+                           _stream(pos))
+    _check("rope_tables", st)
+    return sin_out, cos_out
+
+
+# --------------------------------------------------------------------------- shared marshalling
+def _strides(t: torch.Tensor, layout: str):
+    """{batch, token, head, dim} element strides for a BNSD / BSND / packed TND tensor."""
+    if layout == "BNSD":
+        return (t.stride(0), t.stride(2), t.stride(1), t.stride(3))
+    if layout == "BSND":
+        return (t.stride(0), t.stride(1), t.stride(2), t.stride(3))
+    if layout == "TND":
+        return (0, t.stride(0), t.stride(1), t.stride(2))
+    raise ValueError(f"unknown layout {layout}")
+
+
+def _dims(t: torch.Tensor, layout: str):
+    """(batch, seq, heads, head_dim) of a tensor in the given layout (batch=1, seq=T for TND)."""
+    if layout == "BNSD":
+        return t.shape[0], t.shape[2], t.shape[1], t.shape[3]
+    if layout == "BSND":
+        return t.shape[0], t.shape[1], t.shape[2], t.shape[3]
+    if layout == "TND":
+        return 1, t.shape[0], t.shape[1], t.shape[2]
+    raise ValueError(f"unknown layout {layout}")
+
+
+def _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows, batch=None):
+    if (cu_seqlens is None) != (layout != "TND"):
+        raise ValueError("packed TND layout goes with cu_seqlens, dense layouts without")
+    p = RopeAttnParams()
+    p.struct_size = ctypes.sizeof(RopeAttnParams)
+    p.dtype = DTYPE.get(q.dtype, -1)
+    p.q, p.k = q.data_ptr(), k.data_ptr()
+    B, S, Hq, D = _dims(q, layout)
+    Bk, Sk, Hkv, Dk = _dims(k, layout)
+    if (Bk, Sk, Dk) != (B, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k must agree in batch, tokens, head_dim and dtype")
+    p.hq, p.hkv, p.head_dim = Hq, Hkv, D
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        p.batch = cu_seqlens.numel() - 1
+        p.cu_seqlens = cu_seqlens.data_ptr()
+        p.max_seqlen = int(max_seqlen)
+        p.ntokens = S
+        p.seqlen = 0
+    else:
+        p.batch, p.seqlen, p.ntokens = B, S, B * S
+    p.q_stride[:] = _strides(q, layout)
+    p.k_stride[:] = _strides(k, layout)
+    if cos is not None or sin is not None:
+        if cos is None or sin is None:
+            raise ValueError("cos and sin go together")
+        if not (cos.is_contiguous() and sin.is_contiguous()) or cos.shape != sin.shape or cos.shape[-1] != D:
+            raise ValueError("tables must be contiguous [rows, head_dim]")
+        p.cos, p.sin = cos.data_ptr(), sin.data_ptr()
+        p.table_dtype = DTYPE.get(cos.dtype, -1)
+        if sin.dtype != cos.dtype:
+            raise ValueError("cos and sin must share a dtype")
+        rows_needed = (S if cu_seqlens is not None else
+                       (S if table_seq_rows == 0 else B * table_seq_rows))
+        if cos.shape[0] < rows_needed:
+            raise ValueError(f"tables have {cos.shape[0]} rows, {rows_needed} needed")
+    p.table_seq_rows = int(table_seq_rows)
+    return p
+
+
+# --------------------------------------------------------------------------- rope_qk
+def rope_qk(q: torch.Tensor, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, *, layout: str = "BNSD",
+            cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None, table_seq_rows: int = 0,
+            out_q: Optional[torch.Tensor] = None, out_k: Optional[torch.Tensor] = None):
+    """Rotated (q', k') written to out_q / out_k (new tensors like q / k by default)."""
+    _need_cuda(q, k, cos, sin, cu_seqlens, out_q, out_k)
+    p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    out_q = torch.empty_like(q) if out_q is None else out_q
+    out_k = torch.empty_like(k) if out_k is None else out_k
+    if out_q.shape != q.shape or out_k.shape != k.shape or _strides(out_q, layout) != _strides(q, layout) \
+            or _strides(out_k, layout) != _strides(k, layout):
+        raise ValueError("out_q/out_k must have the shapes and strides of q/k")
+    p.out_q, p.out_k = out_q.data_ptr(), out_k.data_ptr()
+    _check("rope_qk", lib().rope_qk(ctypes.byref(p), _stream(q)))
+    return out_q, out_k
+
+
+# --------------------------------------------------------------------------- rope_flash_attn_fwd
+def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: Optional[torch.Tensor] = None,
+                        sin: Optional[torch.Tensor] = None, *, causal: bool = True,
+                        softmax_scale: Optional[float] = None, layout: str = "BNSD",
+                        cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                        table_seq_rows: int = 0, return_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Attention output (and lse [hq, ntokens] float32 if asked); cos = sin = None: no rotation."""
+    _need_cuda(q, k, v, cos, sin, cu_seqlens, out)
+    p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    if v.shape != k.shape or v.dtype != q.dtype:
+        raise ValueError("v must match k")
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    p.v, p.out = v.data_ptr(), out.data_ptr()
+    p.v_stride[:] = _strides(v, layout)
+    p.o_stride[:] = _strides(out, layout)
+    p.causal = 1 if causal else 0
+    p.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / q.shape[-1] ** 0.5)
+    lse = None
+    if return_lse:
+        lse = torch.empty((p.hq, p.ntokens), dtype=torch.float32, device=q.device)
+        p.lse = lse.data_ptr()
+    _check("rope_flash_attn_fwd", lib().rope_flash_attn_fwd(ctypes.byref(p), _stream(q)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,181 @@
+// C ABI of librope_fa: host-side validation and dispatch.
+//
+// Every check here runs before any HIP call, so an invalid call enqueues nothing and
+// writes nothing.  Constraint sources: the [DynamicNTKOperation] page, section 约束说明
+// (table limits) and 参数列表 (UNDEFINED output dtype is unusable); the [RoPE-fusion
+// blog]'s warning that a fused operator must not silently fall back (here: unsupported
+// shapes, strides and alignments are errors).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "common.h"
+#include "rope_fa.h"
+
+namespace ropefa {
+hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
+                              int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype,
+                              void* sin_out, void* cos_out, hipStream_t stream);
+hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
+hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
+}  // namespace ropefa
+
+using ropefa::dtype_bytes;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(rope_dtype dt) { return dt == ROPE_DT_F16 || dt == ROPE_DT_BF16 || dt == ROPE_DT_F32; }
+
+// Strides {batch, token, head, dim}: dim must be 1; the others non-negative and 16-byte multiples.
+rope_status check_strides(const int64_t s[4], int elem_bytes, bool varlen) {
+    if (s[3] != 1) return ROPE_ERR_UNSUPPORTED;
+    for (int i = 0; i < 3; ++i) {
+        if (varlen && i == 0) continue;
+        if (s[i] < 0) return ROPE_ERR_SHAPE;
+        if ((s[i] * elem_bytes) % 16 != 0) return ROPE_ERR_UNSUPPORTED;
+    }
+    return ROPE_OK;
+}
+
+// Checks shared by rope_qk and rope_flash_attn_fwd.
+rope_status check_params(const rope_attn_params* p, bool attention) {
+    if (!p) return ROPE_ERR_NULL;
+    if (p->struct_size != sizeof(rope_attn_params)) return ROPE_ERR_ABI;
+    for (unsigned char c : p->rsv)
+        if (c) return ROPE_ERR_ABI;
+    if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
+    if (!p->q || !p->k) return ROPE_ERR_NULL;
+    if (attention) {
+        if (!p->v || !p->out) return ROPE_ERR_NULL;
+    } else {
+        if (!p->out_q || !p->out_k) return ROPE_ERR_NULL;
+        if (!p->cos || !p->sin) return ROPE_ERR_NULL;
+    }
+    if ((p->cos == nullptr) != (p->sin == nullptr)) return ROPE_ERR_NULL;
+    if (p->batch <= 0 || p->hq <= 0 || p->hkv <= 0 || p->head_dim <= 0) return ROPE_ERR_SHAPE;
+    if (p->hq % p->hkv != 0) return ROPE_ERR_SHAPE;
+    const bool varlen = p->cu_seqlens != nullptr;
+    if (varlen) {
+        if (p->max_seqlen <= 0 || p->ntokens <= 0) return ROPE_ERR_SHAPE;
+        if (p->max_seqlen > p->ntokens) return ROPE_ERR_SHAPE;
+    } else {
+        if (p->seqlen <= 0) return ROPE_ERR_SHAPE;
+        const int64_t rows = (int64_t)p->batch * p->seqlen;
+        if (rows > INT32_MAX) return ROPE_ERR_LIMIT;
+        if (p->ntokens != 0 && p->ntokens != rows) return ROPE_ERR_SHAPE;
+        if (p->table_seq_rows < 0) return ROPE_ERR_SHAPE;
+        if (p->table_seq_rows > 0 && p->table_seq_rows < p->seqlen) return ROPE_ERR_SHAPE;
+    }
+    if (attention) {
+        if (p->head_dim != 64 && p->head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+        if (p->dtype == ROPE_DT_F32 && p->head_dim != 64) return ROPE_ERR_UNSUPPORTED;
+        if (p->causal != 0 && p->causal != 1) return ROPE_ERR_SHAPE;
+        if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f)) return ROPE_ERR_SHAPE;
+        if (p->batch > 65535) return ROPE_ERR_LIMIT;
+    } else {
+        if (p->head_dim % 32 != 0) return ROPE_ERR_UNSUPPORTED;
+        if (p->head_dim > ROPE_MAX_HEAD_SIZE) return ROPE_ERR_LIMIT;
+    }
+    if (p->cos && p->table_dtype != p->dtype) return ROPE_ERR_DTYPE;
+    const int eb = dtype_bytes(p->dtype);
+    rope_status st;
+    if ((st = check_strides(p->q_stride, eb, varlen)) != ROPE_OK) return st;
+    if ((st = check_strides(p->k_stride, eb, varlen)) != ROPE_OK) return st;
+    if (attention) {
+        if ((st = check_strides(p->v_stride, eb, varlen)) != ROPE_OK) return st;
+        if ((st = check_strides(p->o_stride, eb, varlen)) != ROPE_OK) return st;
+    }
+    if (!aligned16(p->q) || !aligned16(p->k)) return ROPE_ERR_UNSUPPORTED;
+    if (attention && (!aligned16(p->v) || !aligned16(p->out))) return ROPE_ERR_UNSUPPORTED;
+    if (!attention && (!aligned16(p->out_q) || !aligned16(p->out_k))) return ROPE_ERR_UNSUPPORTED;
+    if (p->cos && (!aligned16(p->cos) || !aligned16(p->sin))) return ROPE_ERR_UNSUPPORTED;
+    if (p->lse && (reinterpret_cast<uintptr_t>(p->lse) & 3u)) return ROPE_ERR_UNSUPPORTED;
+    if (varlen && (reinterpret_cast<uintptr_t>(p->cu_seqlens) & 3u)) return ROPE_ERR_UNSUPPORTED;
+    return ROPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rope_status_str(rope_status s) {
+    switch (s) {
+        case ROPE_OK: return "ROPE_OK";
+        case ROPE_ERR_NULL: return "ROPE_ERR_NULL";
+        case ROPE_ERR_SHAPE: return "ROPE_ERR_SHAPE";
+        case ROPE_ERR_DTYPE: return "ROPE_ERR_DTYPE";
+        case ROPE_ERR_LIMIT: return "ROPE_ERR_LIMIT";
+        case ROPE_ERR_UNSUPPORTED: return "ROPE_ERR_UNSUPPORTED";
+        case ROPE_ERR_ABI: return "ROPE_ERR_ABI";
+        case ROPE_ERR_HIP: return "ROPE_ERR_HIP";
+    }
+    return "ROPE_ERR_UNKNOWN";
+}
+
+int32_t rope_abi_version(void) { return ROPE_FA_ABI_VERSION; }
+
+uint32_t rope_attn_params_size(void) { return (uint32_t)sizeof(rope_attn_params); }
+
+rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_lens, int32_t batch, int32_t trained_len,
+                          float* out) {
+    if (!out) return ROPE_ERR_NULL;
+    if (trained_len > 0 && !seq_lens) return ROPE_ERR_NULL;
+    if (!(std::isfinite(base) && base > 0.0)) return ROPE_ERR_SHAPE;
+    if (head_size <= 0 || head_size % 2 != 0 || batch <= 0) return ROPE_ERR_SHAPE;
+    if (head_size > ROPE_MAX_HEAD_SIZE || batch > ROPE_MAX_BATCH) return ROPE_ERR_LIMIT;
+    if (seq_lens)
+        for (int b = 0; b < batch; ++b)
+            if (seq_lens[b] <= 0) return ROPE_ERR_SHAPE;
+    const int half = head_size / 2;
+    for (int b = 0; b < batch; ++b) {
+        double base_b = base;
+        if (trained_len > 0 && seq_lens[b] > trained_len)
+            base_b = base * std::pow((double)seq_lens[b] / (double)trained_len,
+                                     (double)head_size / (double)(head_size - 2));
+        for (int i = 0; i < half; ++i)
+            out[(int64_t)b * half + i] = (float)(1.0 / std::pow(base_b, (double)(2 * i) / (double)head_size));
+    }
+    return ROPE_OK;
+}
+
+rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
+                        int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype, void* sin_out,
+                        void* cos_out, void* hip_stream) {
+    if (!pos || !inv_freq || !seq_lens || !sin_out || !cos_out) return ROPE_ERR_NULL;
+    if (batch <= 0 || ntokens <= 0 || head_size <= 0) return ROPE_ERR_SHAPE;
+    if (batch > ROPE_MAX_BATCH || ntokens > ROPE_MAX_NTOKENS) return ROPE_ERR_LIMIT;
+    if (head_size > ROPE_MAX_HEAD_SIZE || head_size % 32 != 0) return ROPE_ERR_LIMIT;
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (seq_lens[b] <= 0) return ROPE_ERR_SHAPE;
+        total += seq_lens[b];
+    }
+    if (total != ntokens) return ROPE_ERR_SHAPE;
+    if (!(std::isfinite(pos_scale) && pos_scale > 0.0f)) return ROPE_ERR_SHAPE;
+    if (!valid_dtype(out_dtype)) return ROPE_ERR_DTYPE;
+    if (!aligned16(inv_freq) || !aligned16(sin_out) || !aligned16(cos_out)) return ROPE_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(pos) & 3u) return ROPE_ERR_UNSUPPORTED;
+    const hipError_t e = ropefa::launch_rope_tables(pos, inv_freq, seq_lens, batch, ntokens, head_size, pos_scale,
+                                                    out_dtype, sin_out, cos_out, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_qk(const rope_attn_params* p, void* hip_stream) {
+    const rope_status st = check_params(p, false);
+    if (st != ROPE_OK) return st;
+    const hipError_t e = ropefa::launch_rope_qk(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream) {
+    const rope_status st = check_params(p, true);
+    if (st != ROPE_OK) return st;
+    const hipError_t e = ropefa::launch_flash_fwd(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+"""Seeded synthetic workloads shared by the tests, the benchmark and the smoke check.
+
+This module draws inputs only: shapes, random Q/K/V, positions and sequence lengths.
+It holds none of the method's arithmetic (no inverse frequencies, tables, rotations or
+attention), so both the GPU path and the CPU oracle can consume what it produces.
+
+Recipe: numpy Generator(PCG64(seed)); for varlen workloads the sequence lengths are
+drawn first as integers in [lo, hi] inclusive; then Q, K, V ~ N(0, 1) in float32, in
+that order, rounded to the workload dtype by torch's CPU cast (round to nearest even).
+Dense tensors are BNSD [batch, heads, seq, head_dim]; varlen tensors are packed
+[ntokens, heads, head_dim].  Positions are 0 .. L-1 for every sequence.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str                      # "f32" | "bf16" | "f16"
+    batch: int
+    hq: int
+    hkv: int
+    head_dim: int
+    seqlen: int = 0                 # dense: tokens per sequence
+    varlen: bool = False
+    len_range: Tuple[int, int] = (0, 0)   # varlen: inclusive bounds of the drawn lengths
+    base: float = 10000.0
+    trained_len: Optional[int] = None     # dynamic NTK above this length (None: off)
+    pos_scale: float = 1.0                # linear rope_scaling_factor
+    causal: bool = True
+    seed: int = 0
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(self.head_dim) ** 0.5
+
+    @property
+    def torch_dtype(self):
+        return TORCH_DTYPES[self.dtype]
+
+
+# The five workloads of the method's headline comparison, by shape only (random weights).
+CONFIGS = {
+    1: Workload("tiny-fp32 B1 H4/4 D64 S128", "f32", 1, 4, 4, 64, seqlen=128, base=1e4, seed=1001),
+    2: Workload("qwen7b-like B4 H32/32 D128 S2048", "bf16", 4, 32, 32, 128, seqlen=2048, base=1e4, seed=1002),
+    3: Workload("llama3-8b-like GQA B2 H32/8 D128 S4096", "bf16", 2, 32, 8, 128, seqlen=4096, base=5e5, seed=1003),
+    4: Workload("varlen-ntk 8 seqs L~U[512,8192] H32/32 D128 fp16", "f16", 8, 32, 32, 128, varlen=True,
+                len_range=(512, 8192), base=1e4, trained_len=4096, seed=1004),
+    5: Workload("qwen72b-like long B1 H64/8 D128 S16384 s=2", "bf16", 1, 64, 8, 128, seqlen=16384, base=1e6,
+                pos_scale=2.0, seed=1005),
+}
+
+# Reduced shapes for full-output parity: several 64-key tiles, ragged tails, same features.
+SMALL = {
+    1: CONFIGS[1],
+    2: Workload("small qwen7b-like B2 H4/4 D128 S300", "bf16", 2, 4, 4, 128, seqlen=300, base=1e4, seed=2002),
+    3: Workload("small llama3-like GQA B1 H8/2 D128 S333", "bf16", 1, 8, 2, 128, seqlen=333, base=5e5, seed=2003),
+    4: Workload("small varlen-ntk 4 seqs L~U[1,300] H4/4 D128 fp16", "f16", 4, 4, 4, 128, varlen=True,
+                len_range=(1, 300), base=1e4, trained_len=128, seed=2004),
+    5: Workload("small long-like B1 H16/2 D128 S520 s=2", "bf16", 1, 16, 2, 128, seqlen=520, base=1e6,
+                pos_scale=2.0, seed=2005),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    workload: Workload
+    q: torch.Tensor          # CPU, workload dtype; BNSD (dense) or [T, Hq, D] (varlen)
+    k: torch.Tensor
+    v: torch.Tensor
+    seq_lens: np.ndarray     # int32 [batch]
+    pos: np.ndarray          # int32 [ntokens], 0..L-1 per sequence
+
+    @property
+    def ntokens(self) -> int:
+        return int(self.seq_lens.sum())
+
+    def packed(self):
+        """(q, k, v) as float64 numpy arrays in packed [T, H, D] token order (for the oracle)."""
+        def pk(x):
+            x = x.to(torch.float64)
+            if not self.workload.varlen:
+                x = x.permute(0, 2, 1, 3).reshape(-1, x.shape[1], x.shape[3])
+            return x.numpy()
+        return pk(self.q), pk(self.k), pk(self.v)
+
+
+def _normal(rng: np.random.Generator, shape, dtype) -> torch.Tensor:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return torch.from_numpy(x).to(dtype)
+
+
+def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    if w.varlen:
+        lo, hi = w.len_range
+        seq_lens = rng.integers(lo, hi + 1, size=w.batch).astype(np.int32)
+        T = int(seq_lens.sum())
+        qs, ks = (T, w.hq, w.head_dim), (T, w.hkv, w.head_dim)
+    else:
+        seq_lens = np.full(w.batch, w.seqlen, dtype=np.int32)
+        qs, ks = (w.batch, w.hq, w.seqlen, w.head_dim), (w.batch, w.hkv, w.seqlen, w.head_dim)
+    q = _normal(rng, qs, w.torch_dtype)
+    k = _normal(rng, ks, w.torch_dtype)
+    v = _normal(rng, ks, w.torch_dtype)
+    pos = np.concatenate([np.arange(L, dtype=np.int32) for L in seq_lens.tolist()])
+    return Inputs(w, q, k, v, seq_lens, pos)
+
+
+def cu_seqlens(seq_lens) -> np.ndarray:
+    """[batch + 1] int32 prefix sums starting at 0 (index bookkeeping for packed batches)."""
+    return np.concatenate([[0], np.cumsum(np.asarray(seq_lens, dtype=np.int64))]).astype(np.int32)
+
+
+def causal_flops(w: Workload, seq_lens) -> float:
+    """Algorithmic FLOPs of causal attention: 4*Hq*L^2*D/2 per sequence (QK^T and PV)."""
+    per = sum(float(L) * float(L) for L in np.asarray(seq_lens).tolist())
+    f = 4.0 * w.hq * per * w.head_dim
+    return f / 2.0 if w.causal else f

@@ -16,3 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session")
+def ropelib():
+    """The built librope_fa.so (built first if absent), loaded through the binding."""
+    import rope_flashattention_amd as rfa
+    if not os.path.exists(rfa.LIB_PATH):
+        from rope_flashattention_amd.build import build
+        build()
+    return rfa.lib()

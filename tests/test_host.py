@@ -1,0 +1,239 @@
+"""CPU-only tests of the C ABI: symbols, struct layout, host validation, host inv_freq.
+
+Every call here is rejected by host validation before any HIP call, or is host-only
+(rope_inv_freq, rope_status_str, ...), so nothing touches a GPU.  Device pointers
+passed here are dummies that the library never dereferences on these paths.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import rope_flashattention_amd as rfa
+from rope_flashattention_amd import RopeAttnParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rope_fa.h")
+FAKE = 0x10000  # 16-byte aligned dummy device address, never dereferenced here
+
+# Dummy device pointers are only ever handed to the library where no GPU exists, so a
+# validation slip can never turn into a launch on a real device.
+import torch  # noqa: E402
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="dummy device pointers: CPU-only test")
+
+ST = {v: k for k, v in rfa.STATUS.items()}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(rope_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(ropelib):
+    names = declared_functions()
+    assert {"rope_tables", "rope_qk", "rope_flash_attn_fwd", "rope_inv_freq"} <= set(names)
+    for n in names:
+        assert hasattr(ropelib, n), n
+
+
+def test_abi_version_and_struct_size(ropelib):
+    assert ropelib.rope_abi_version() == 1
+    assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
+    for s, name in rfa.STATUS.items():
+        assert ropelib.rope_status_str(s).decode() == name
+
+
+# --------------------------------------------------------------------------- rope_inv_freq
+@pytest.mark.parametrize("base,D", [(1e4, 64), (1e4, 128), (5e5, 128), (1e6, 128), (1e4, 2048)])
+def test_inv_freq_matches_oracle_bitwise(ropelib, base, D):
+    got = rfa.inv_freq(base, D)
+    want = orc.inv_freq(base, D)
+    assert got.dtype == np.float32 and np.array_equal(got[0], want)
+
+
+def test_inv_freq_ntk_matches_oracle_bitwise(ropelib):
+    seq_lens = [512, 4096, 4097, 8192, 6000, 1]
+    got = rfa.inv_freq(1e4, 128, seq_lens, trained_len=4096)
+    want = orc.inv_freq_per_sequence(1e4, seq_lens, 128, 4096)
+    assert np.array_equal(got, want)
+
+
+def test_inv_freq_errors(ropelib):
+    L = ropelib
+    out = np.empty(64, dtype=np.float32)
+    sl = np.array([10], dtype=np.int32)
+    assert L.rope_inv_freq(1e4, 128, None, 1, 0, None) == ST["ROPE_ERR_NULL"]
+    assert L.rope_inv_freq(1e4, 128, None, 1, 100, out.ctypes.data) == ST["ROPE_ERR_NULL"]
+    assert L.rope_inv_freq(-1.0, 128, None, 1, 0, out.ctypes.data) == ST["ROPE_ERR_SHAPE"]
+    assert L.rope_inv_freq(float("inf"), 128, None, 1, 0, out.ctypes.data) == ST["ROPE_ERR_SHAPE"]
+    assert L.rope_inv_freq(1e4, 127, None, 1, 0, out.ctypes.data) == ST["ROPE_ERR_SHAPE"]
+    assert L.rope_inv_freq(1e4, 4096, None, 1, 0, out.ctypes.data) == ST["ROPE_ERR_LIMIT"]
+    assert L.rope_inv_freq(1e4, 128, None, 17, 0, out.ctypes.data) == ST["ROPE_ERR_LIMIT"]
+    bad = np.array([0], dtype=np.int32)
+    assert L.rope_inv_freq(1e4, 128, bad.ctypes.data, 1, 100, out.ctypes.data) == ST["ROPE_ERR_SHAPE"]
+    assert L.rope_inv_freq(1e4, 128, sl.ctypes.data, 1, 100, out.ctypes.data) == 0
+
+
+# --------------------------------------------------------------------------- rope_tables validation
+def call_tables(L, pos=FAKE, f=FAKE, seq_lens=(4, 4), batch=None, ntokens=8, head_size=128, scale=1.0,
+                dt=2, so=FAKE, co=FAKE):
+    sl = np.asarray(seq_lens if seq_lens is not None else (4, 4), dtype=np.int32)
+    batch = sl.size if batch is None else batch
+    return L.rope_tables(pos, f, sl.ctypes.data if seq_lens is not None else None, batch, ntokens, head_size,
+                         scale, dt, so, co, None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), "ROPE_ERR_NULL"),
+    (dict(f=None), "ROPE_ERR_NULL"),
+    (dict(seq_lens=None), "ROPE_ERR_NULL"),
+    (dict(so=None), "ROPE_ERR_NULL"),
+    (dict(co=None), "ROPE_ERR_NULL"),
+    (dict(dt=0), "ROPE_ERR_DTYPE"),                      # UNDEFINED is unusable
+    (dict(dt=9), "ROPE_ERR_DTYPE"),
+    (dict(head_size=100), "ROPE_ERR_LIMIT"),             # not a multiple of 32
+    (dict(head_size=2080), "ROPE_ERR_LIMIT"),            # > 2048
+    (dict(head_size=0), "ROPE_ERR_SHAPE"),
+    (dict(seq_lens=[1] * 17, ntokens=17), "ROPE_ERR_LIMIT"),    # batch > 16
+    (dict(seq_lens=[128000, 128001], ntokens=256001), "ROPE_ERR_LIMIT"),
+    (dict(ntokens=9), "ROPE_ERR_SHAPE"),                 # sum(seq_lens) != ntokens
+    (dict(seq_lens=[8, 0], ntokens=8), "ROPE_ERR_SHAPE"),
+    (dict(seq_lens=[9, -1], ntokens=8), "ROPE_ERR_SHAPE"),
+    (dict(batch=0), "ROPE_ERR_SHAPE"),
+    (dict(scale=0.0), "ROPE_ERR_SHAPE"),
+    (dict(scale=float("nan")), "ROPE_ERR_SHAPE"),
+    (dict(so=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),         # misaligned output
+    (dict(f=FAKE + 4), "ROPE_ERR_UNSUPPORTED"),
+    (dict(pos=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
+])
+def test_rope_tables_rejects(ropelib, kw, status):
+    assert call_tables(ropelib, **kw) == ST[status]
+
+
+# --------------------------------------------------------------------------- rope_qk / attention validation
+def valid_params(attention=True, dtype=2, D=128, hq=8, hkv=2, B=2, S=100):
+    p = RopeAttnParams()
+    p.struct_size = ctypes.sizeof(RopeAttnParams)
+    p.dtype = dtype
+    p.q = p.k = p.v = p.out = p.out_q = p.out_k = FAKE
+    p.batch, p.hq, p.hkv, p.head_dim, p.seqlen, p.ntokens = B, hq, hkv, D, S, B * S
+    p.causal = 1
+    for name, H in (("q_stride", hq), ("k_stride", hkv), ("v_stride", hkv), ("o_stride", hq)):
+        getattr(p, name)[:] = (H * S * D, D, S * D, 1)   # BNSD
+    p.cos = p.sin = FAKE
+    p.table_dtype = dtype
+    p.softmax_scale = 1.0 / math.sqrt(D)
+    return p
+
+
+def mutate(p, **kw):
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(p, k)[:] = v
+        elif k == "rsv":
+            p.rsv[3] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+BAD_COMMON = [
+    (dict(struct_size=8), "ROPE_ERR_ABI"),
+    (dict(rsv=1), "ROPE_ERR_ABI"),
+    (dict(dtype=0), "ROPE_ERR_DTYPE"),
+    (dict(dtype=7), "ROPE_ERR_DTYPE"),
+    (dict(q=None), "ROPE_ERR_NULL"),
+    (dict(k=None), "ROPE_ERR_NULL"),
+    (dict(sin=None), "ROPE_ERR_NULL"),
+    (dict(hq=6, hkv=4), "ROPE_ERR_SHAPE"),          # hq % hkv != 0
+    (dict(hq=0), "ROPE_ERR_SHAPE"),
+    (dict(batch=0), "ROPE_ERR_SHAPE"),
+    (dict(seqlen=0), "ROPE_ERR_SHAPE"),
+    (dict(ntokens=7), "ROPE_ERR_SHAPE"),
+    (dict(table_seq_rows=50), "ROPE_ERR_SHAPE"),    # fewer rows than seqlen
+    (dict(table_dtype=1), "ROPE_ERR_DTYPE"),        # table dtype differs from q
+    (dict(q_stride=(8 * 100 * 128, 128, 100 * 128, 2)), "ROPE_ERR_UNSUPPORTED"),   # head_dim stride != 1
+    (dict(k_stride=(2 * 100 * 128, 131, 100 * 128, 1)), "ROPE_ERR_UNSUPPORTED"),   # 16-byte rows
+    (dict(q=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
+    (dict(cos=FAKE + 4), "ROPE_ERR_UNSUPPORTED"),
+]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", BAD_COMMON + [
+    (dict(v=None), "ROPE_ERR_NULL"),
+    (dict(out=None), "ROPE_ERR_NULL"),
+    (dict(head_dim=96), "ROPE_ERR_UNSUPPORTED"),    # attention serves 64 and 128 only
+    (dict(head_dim=256), "ROPE_ERR_UNSUPPORTED"),
+    (dict(causal=2), "ROPE_ERR_SHAPE"),
+    (dict(softmax_scale=0.0), "ROPE_ERR_SHAPE"),
+    (dict(softmax_scale=float("inf")), "ROPE_ERR_SHAPE"),
+    (dict(o_stride=(8 * 100 * 128, 128, 100 * 128, 3)), "ROPE_ERR_UNSUPPORTED"),
+    (dict(out=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
+    (dict(lse=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
+    (dict(cu_seqlens=FAKE, max_seqlen=0), "ROPE_ERR_SHAPE"),
+    (dict(cu_seqlens=FAKE, max_seqlen=300, ntokens=200), "ROPE_ERR_SHAPE"),
+])
+def test_rope_flash_attn_fwd_rejects(ropelib, kw, status):
+    p = mutate(valid_params(), **kw)
+    assert ropelib.rope_flash_attn_fwd(ctypes.byref(p), None) == ST[status]
+
+
+@no_gpu_only
+def test_fp32_attention_head_dim(ropelib):
+    p = valid_params(dtype=3, D=128)
+    assert ropelib.rope_flash_attn_fwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", BAD_COMMON + [
+    (dict(out_q=None), "ROPE_ERR_NULL"),
+    (dict(out_k=None), "ROPE_ERR_NULL"),
+    (dict(cos=None, sin=None), "ROPE_ERR_NULL"),    # the Rope op needs its tables
+    (dict(head_dim=48), "ROPE_ERR_UNSUPPORTED"),
+    (dict(head_dim=4096), "ROPE_ERR_LIMIT"),
+    (dict(out_k=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
+])
+def test_rope_qk_rejects(ropelib, kw, status):
+    p = mutate(valid_params(attention=False), **kw)
+    assert ropelib.rope_qk(ctypes.byref(p), None) == ST[status]
+
+
+@no_gpu_only
+def test_null_params(ropelib):
+    assert ropelib.rope_qk(None, None) == ST["ROPE_ERR_NULL"]
+    assert ropelib.rope_flash_attn_fwd(None, None) == ST["ROPE_ERR_NULL"]
+
+
+def test_binding_refuses_cpu_tensors(ropelib):
+    import torch
+    q = torch.zeros(1, 4, 8, 64)
+    with pytest.raises(ValueError):
+        rfa.rope_flash_attn_fwd(q, q, q)
+
+
+# --------------------------------------------------------------------------- sin/cos constants
+def test_sincos_constants_derive_from_pi():
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 60
+    src = open(os.path.join(ROOT, "rope_flashattention_amd", "csrc", "rope_tables.hip")).read()
+
+    def const(name):
+        m = re.search(r"constexpr float %s = ([-0-9a-fx.p+]+)f;" % name, src)
+        return float.fromhex(m.group(1))
+
+    f32 = lambda x: float(np.float32(float(x)))
+    hi = f32(mpmath.pi / 2)
+    mid = f32(mpmath.pi / 2 - hi)
+    lo = f32(mpmath.pi / 2 - hi - mid)
+    assert const("kHalfPiHi") == hi
+    assert const("kHalfPiMid") == mid
+    assert const("kHalfPiLo") == lo
+    assert const("kTwoOverPi") == f32(2 / mpmath.pi)
