@@ -77,7 +77,7 @@ def time_events(fn, reps, torch):
 
 
 def cpu_baseline(inp, budget_s):
-    """The oracle as it stands on sequence 0, one q head at a time, until the budget is spent."""
+    """The oracle as it stands, one (sequence, q head) at a time, until the budget is spent."""
     import numpy as np
     import oracle as orc
     try:
@@ -86,25 +86,30 @@ def cpu_baseline(inp, budget_s):
     except Exception:  # threadpoolctl missing: report the affinity set
         threads = len(os.sched_getaffinity(0))
     w = inp.workload
-    S = int(inp.seq_lens[0])
     q, k, v = inp.packed()
-    q, k, v = q[:S], k[:S], v[:S]
+    starts = orc.segment_starts(inp.seq_lens)
     g = w.hq // w.hkv
     t0 = time.perf_counter()
-    f = orc.inv_freq_per_sequence(w.base, inp.seq_lens[:1], w.head_dim, w.trained_len)
-    s, c = orc.rope_tables(inp.pos[:S], f, inp.seq_lens[:1], w.pos_scale)
-    s, c = orc.round_rne(s, w.dtype), orc.round_rne(c, w.dtype)
-    heads = 0
-    while heads < w.hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
-        h = heads
-        orc.rope_attention(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1], c, s, [S],
-                           w.softmax_scale, w.causal)
-        heads += 1
+    flops, done = 0.0, 0
+    for b in range(w.batch):
+        s0, S = int(starts[b]), int(inp.seq_lens[b])
+        f = orc.inv_freq_per_sequence(w.base, inp.seq_lens[b:b + 1], w.head_dim, w.trained_len)
+        sn, cs = orc.rope_tables(inp.pos[s0:s0 + S], f, inp.seq_lens[b:b + 1], w.pos_scale)
+        sn, cs = orc.round_rne(sn, w.dtype), orc.round_rne(cs, w.dtype)
+        for h in range(w.hq):
+            sl = slice(s0, s0 + S)
+            orc.rope_attention(q[sl, h:h + 1], k[sl, h // g:h // g + 1], v[sl, h // g:h // g + 1], cs, sn, [S],
+                               w.softmax_scale, w.causal)
+            flops += 4.0 * S * S * w.head_dim / (2.0 if w.causal else 1.0)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
     dt = time.perf_counter() - t0
-    flops = 4.0 * heads * S * S * w.head_dim / (2.0 if w.causal else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"sequence 0 (S={S}), {heads} of {w.hq} q heads, full causal rows, tables included; "
-                      f"{dt:.1f} s wall, numpy float64 with {threads} BLAS threads"}
+            "sample": f"{done} of {w.batch * w.hq} (sequence, q head) pairs in order, full causal rows, "
+                      f"tables included; {dt:.1f} s wall, numpy float64 with {threads} BLAS threads"}
 
 
 def main():
@@ -116,6 +121,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the table/rope_qk/unfused measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (scales HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,8 +138,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    rfa.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": a.numel() * 4,
+                          "copy_calibration_bytes_written_per_launch": b.numel() * 4}), flush=True)
+        return
+    rfa.lib()
     w = wl.CONFIGS[args.config]
     inp = wl.generate(w)
     D = w.head_dim

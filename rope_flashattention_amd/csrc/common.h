@@ -15,6 +15,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -28,8 +31,13 @@ template <> struct Elem<__bf16> {
     static constexpr int bytes = 2;
     __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    // one packed round-to-nearest-even conversion of two floats
     __device__ static __forceinline__ uint32_t pack(float a, float b) {
-        return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    }
+    // a.lo*b.lo + a.hi*b.hi + c in float32
+    __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
     }
 };
 template <> struct Elem<_Float16> {
@@ -37,7 +45,10 @@ template <> struct Elem<_Float16> {
     __device__ static __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
     __device__ static __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
     __device__ static __forceinline__ uint32_t pack(float a, float b) {
-        return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+    }
+    __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
     }
 };
 template <> struct Elem<float> { static constexpr int bytes = 4; };
@@ -129,6 +140,28 @@ __device__ __forceinline__ void rotate_pair(float (&x)[8], float (&y)[8], const 
         const float xv = x[e], yv = y[e];
         x[e] = xv * c0[e] - yv * s0[e];
         y[e] = yv * c1[e] + xv * s1[e];
+    }
+}
+
+// The same rotation on packed 16-bit data, 4 dwords (8 elements) per operand, tables in
+// the rotate-half form (one cos/sin value per pair): per element pair (x_j, y_j),
+//   x'_j = dot(x_j, y_j ; c_j, -s_j),   y'_j = dot(x_j, y_j ; s_j, c_j)
+// with v_perm_b32 building the (x_j, y_j) and table pairs and v_dot2 doing the products in
+// float32; results are rounded once to T.
+template <typename T>
+__device__ __forceinline__ void rotate_pair_packed(const u32x4& x, const u32x4& y, const u32x4& c, const u32x4& s,
+                                                   u32x4& xo, u32x4& yo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t xy_e = __builtin_amdgcn_perm(y[i], x[i], 0x05040100u);  // (x_2i,   y_2i)
+        const uint32_t xy_o = __builtin_amdgcn_perm(y[i], x[i], 0x07060302u);  // (x_2i+1, y_2i+1)
+        const uint32_t ns = s[i] ^ 0x80008000u;                                // -s (both halves)
+        const uint32_t cs_e = __builtin_amdgcn_perm(ns, c[i], 0x05040100u);    // (c, -s)
+        const uint32_t cs_o = __builtin_amdgcn_perm(ns, c[i], 0x07060302u);
+        const uint32_t sc_e = __builtin_amdgcn_perm(c[i], s[i], 0x05040100u);  // (s, c)
+        const uint32_t sc_o = __builtin_amdgcn_perm(c[i], s[i], 0x07060302u);
+        xo[i] = Elem<T>::pack(Elem<T>::dot2(xy_e, cs_e, 0.0f), Elem<T>::dot2(xy_o, cs_o, 0.0f));
+        yo[i] = Elem<T>::pack(Elem<T>::dot2(xy_e, sc_e, 0.0f), Elem<T>::dot2(xy_o, sc_o, 0.0f));
     }
 }
 
