@@ -17,7 +17,7 @@ state.  Page key used in the citations:
   功能说明 (function), 算子功能分析 (formula), 输入/输出 (inputs/outputs),
   约束说明 (constraints).
 * [RoPE/GQA tutorial]  smarter.xin/posts/3494b8a4 — section 五 (relative
-  position), 六 (rotation geometry), 十一/十二 (MQA/GQA).
+  position), 六 (rotation geometry), 八 (RMSNorm), 十一/十二 (MQA/GQA).
 
 Readings taken where the pages are silent (also listed in the design notes):
 rotate-half pairing (dims i and i+D/2 share frequency i, from emb = cat(freq,
@@ -51,6 +51,8 @@ __all__ = [
     "round_rne",
     "ulp",
     "DTYPE_FORMATS",
+    "rms_norm",
+    "kv_rms_norm_rope_cache",
 ]
 
 # (precision p incl. the implicit bit, minimum normal exponent emin)
@@ -321,6 +323,40 @@ def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool,
         outs.append((e / l) @ vv[:n_keys])
         lses.append(m + np.log(l))
     return np.stack(outs), np.asarray(lses)
+
+
+# --------------------------------------------------------------------------- KV-cache step
+def rms_norm(x, gamma, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: gamma * x / sqrt(mean(x^2) + eps).
+
+    [RoPE/GQA tutorial, section 八]: scale by the root mean square, no mean subtraction.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64) * x / np.sqrt(ms + float(eps))
+
+
+def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
+    """The fused "RMSNorm, RoPE, write to the KV cache" step for new tokens.
+
+    The [RoPE-fusion blog] (section 五) names this step (kv_rms_norm_rope_cache) without
+    defining it; the reading taken: for every new token t and kv head h,
+      k_cache[slots[t], h] = rope(rms_norm(k[t, h], gamma, eps), cos[t], sin[t])
+      v_cache[slots[t], h] = v[t, h]
+    with rope the Rope-op matrix of ``rope_op_matrix`` and tokens whose slot is negative
+    skipped.  k, v: [T, H, D]; caches: [num_slots, H, D]; returns new float64 caches.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    kn = rms_norm(k, gamma, eps)
+    kr = rotate_tokens(kn, cos, sin)
+    for t, slot in enumerate(np.asarray(slots).tolist()):
+        if slot < 0:
+            continue
+        kc[slot] = kr[t]
+        vc[slot] = np.asarray(v[t], dtype=np.float64)
+    return kc, vc
 
 
 # --------------------------------------------------------------------------- numerics helpers

@@ -328,6 +328,69 @@ def test_ulp_values():
     assert orc.ulp(-0.75, "bf16") == 2**-8
 
 
+# --------------------------------------------------------------------------- RMSNorm + RoPE + cache write
+def check_rms_norm(rms_norm):
+    r = rng(8)
+    # constant vector: |c| is its root mean square
+    g = r.uniform(0.5, 2.0, size=16)
+    y = rms_norm(np.full(16, -3.0), g, 0.0)
+    assert np.max(np.abs(y + g)) < 1e-15
+    # unit weights, no epsilon: the output has root mean square 1 and the input's direction
+    x = r.standard_normal((5, 64))
+    y = rms_norm(x, np.ones(64), 0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(y * y, axis=-1)) - 1.0)) < 1e-14
+    assert np.max(np.abs(y / np.linalg.norm(y, axis=-1, keepdims=True) - x / np.linalg.norm(x, axis=-1, keepdims=True))) < 1e-14
+    # scalar loops, independent of the vectorised form, with epsilon
+    gg = r.uniform(0.5, 2.0, 64)
+    xs = x[2].tolist()
+    ms = sum(v * v for v in xs) / len(xs)
+    want = [gi * v / math.sqrt(ms + 1e-3) for gi, v in zip(gg.tolist(), xs)]
+    assert np.max(np.abs(rms_norm(x[2], gg, 1e-3) - np.array(want))) < 1e-14
+    # rows are independent: a batch gives the rows one by one
+    xb = r.standard_normal((3, 4, 64))
+    yb = rms_norm(xb, gg, 1e-5)
+    assert np.max(np.abs(yb[1, 2] - rms_norm(xb[1, 2], gg, 1e-5))) == 0.0
+
+
+def test_rms_norm():
+    check_rms_norm(orc.rms_norm)
+
+
+def check_kv_cache(kv_rms_norm_rope_cache):
+    r = rng(9)
+    T, H, D, S = 6, 2, 16, 10
+    k = r.standard_normal((T, H, D))
+    v = r.standard_normal((T, H, D))
+    g = r.uniform(0.5, 2.0, D)
+    theta = r.uniform(-3, 3, size=(T, D // 2))
+    emb = np.concatenate([theta, theta], axis=-1)
+    cos, sin = np.cos(emb), np.sin(emb)
+    slots = np.array([3, 7, -1, 0, 9, 5])
+    kc0 = r.standard_normal((S, H, D))
+    vc0 = r.standard_normal((S, H, D))
+    kc, vc = kv_rms_norm_rope_cache(k, v, g, 1e-6, cos, sin, slots, kc0, vc0)
+    untouched = [s for s in range(S) if s not in slots.tolist()]
+    assert np.array_equal(kc[untouched], kc0[untouched]) and np.array_equal(vc[untouched], vc0[untouched])
+    for t, slot in enumerate(slots.tolist()):
+        if slot < 0:
+            continue
+        assert np.array_equal(vc[slot], v[t])
+        for h in range(H):
+            # rotation keeps the normalised row's length: sqrt(sum((g*x/rms)^2))
+            n = np.linalg.norm(g * k[t, h] / math.sqrt(np.mean(k[t, h] ** 2) + 1e-6))
+            assert abs(np.linalg.norm(kc[slot, h]) - n) < 1e-12 * n
+            # and each pair (i, i+D/2) is the normalised pair turned by theta_i
+            y = g * k[t, h] / math.sqrt(np.mean(k[t, h] ** 2) + 1e-6)
+            for i in range(D // 2):
+                c, s_ = math.cos(theta[t, i]), math.sin(theta[t, i])
+                assert abs(kc[slot, h, i] - (c * y[i] - s_ * y[i + D // 2])) < 1e-12
+                assert abs(kc[slot, h, i + D // 2] - (s_ * y[i] + c * y[i + D // 2])) < 1e-12
+
+
+def test_kv_rms_norm_rope_cache():
+    check_kv_cache(orc.kv_rms_norm_rope_cache)
+
+
 # --------------------------------------------------------------------------- planted mistakes
 # Each mutant is one plausible slip; at least one pin above must reject it.
 
@@ -401,6 +464,24 @@ def _mut_attention_transposed(q, k, v, scale, causal=True):
     return P @ np.asarray(v), lse
 
 
+def _mut_rms_norm_no_mean(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return np.asarray(gamma) * x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _mut_kv_cache_norm_after_rope(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
+    # gamma applied after the rotation instead of before it
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    kn = orc.rms_norm(k, np.ones_like(gamma), eps)
+    kr = orc.rotate_tokens(kn, cos, sin) * np.asarray(gamma)
+    for t, slot in enumerate(np.asarray(slots).tolist()):
+        if slot >= 0:
+            kc[slot] = kr[t]
+            vc[slot] = v[t]
+    return kc, vc
+
+
 def _mut_rope_attention_gqa_strided(q, k, v, cos, sin, seq_lens, scale, causal=True):
     hq, hkv = q.shape[1], k.shape[1]
     idx = np.arange(hq) % hkv                      # strided instead of contiguous groups
@@ -427,6 +508,8 @@ def _mut_rope_attention_no_segments(q, k, v, cos, sin, seq_lens, scale, causal=T
     ("softmax over wrong axis", lambda g: check_attention(_mut_attention_transposed)),
     ("GQA strided groups", lambda g: check_rope_attention(_mut_rope_attention_gqa_strided, orc.rope_attention_rows)),
     ("segments ignored", lambda g: check_rope_attention(_mut_rope_attention_no_segments, orc.rope_attention_rows)),
+    ("RMS without the mean", lambda g: check_rms_norm(_mut_rms_norm_no_mean)),
+    ("gamma after the rotation", lambda g: check_kv_cache(_mut_kv_cache_norm_after_rope)),
 ])
 def test_pins_reject_planted_mistakes(name, run, golden_dir):
     with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
