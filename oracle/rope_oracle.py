@@ -344,15 +344,17 @@ def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
       k_cache[slots[t], h] = rope(rms_norm(k[t, h], gamma, eps), cos[t], sin[t])
       v_cache[slots[t], h] = v[t, h]
     with rope the Rope-op matrix of ``rope_op_matrix`` and tokens whose slot is negative
-    skipped.  k, v: [T, H, D]; caches: [num_slots, H, D]; returns new float64 caches.
+    or past the cache skipped.  ``gamma=None`` leaves out the normalisation (RoPE and the
+    cache write only).  k, v: [T, H, D]; caches: [num_slots, H, D]; returns new float64
+    caches.
     """
     k = np.asarray(k, dtype=np.float64)
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
-    kn = rms_norm(k, gamma, eps)
+    kn = k if gamma is None else rms_norm(k, gamma, eps)
     kr = rotate_tokens(kn, cos, sin)
     for t, slot in enumerate(np.asarray(slots).tolist()):
-        if slot < 0:
+        if slot < 0 or slot >= kc.shape[0]:
             continue
         kc[slot] = kr[t]
         vc[slot] = np.asarray(v[t], dtype=np.float64)

@@ -365,14 +365,28 @@ def check_kv_cache(kv_rms_norm_rope_cache):
     theta = r.uniform(-3, 3, size=(T, D // 2))
     emb = np.concatenate([theta, theta], axis=-1)
     cos, sin = np.cos(emb), np.sin(emb)
-    slots = np.array([3, 7, -1, 0, 9, 5])
+    slots = np.array([3, 7, -1, 0, 9, 5, 10])
+    k = np.concatenate([k, r.standard_normal((1, H, D))])
+    v = np.concatenate([v, r.standard_normal((1, H, D))])
+    theta = np.concatenate([theta, r.uniform(-3, 3, size=(1, D // 2))])
+    emb = np.concatenate([theta, theta], axis=-1)
+    cos, sin = np.cos(emb), np.sin(emb)
     kc0 = r.standard_normal((S, H, D))
     vc0 = r.standard_normal((S, H, D))
     kc, vc = kv_rms_norm_rope_cache(k, v, g, 1e-6, cos, sin, slots, kc0, vc0)
+    # slot 10 is past the cache: skipped like -1
     untouched = [s for s in range(S) if s not in slots.tolist()]
+    assert len(untouched) == 5
     assert np.array_equal(kc[untouched], kc0[untouched]) and np.array_equal(vc[untouched], vc0[untouched])
+    # without gamma: pure rotation of the raw row, pair by pair
+    kc2, _ = kv_rms_norm_rope_cache(k, v, None, 1e-6, cos, sin, slots, kc0, vc0)
+    for t, slot in ((0, 3), (5, 5)):
+        for i in range(D // 2):
+            c, s_ = math.cos(theta[t, i]), math.sin(theta[t, i])
+            assert abs(kc2[slot, 1, i] - (c * k[t, 1, i] - s_ * k[t, 1, i + D // 2])) < 1e-12
+            assert abs(kc2[slot, 1, i + D // 2] - (s_ * k[t, 1, i] + c * k[t, 1, i + D // 2])) < 1e-12
     for t, slot in enumerate(slots.tolist()):
-        if slot < 0:
+        if slot < 0 or slot >= S:
             continue
         assert np.array_equal(vc[slot], v[t])
         for h in range(H):
@@ -473,10 +487,10 @@ def _mut_kv_cache_norm_after_rope(k, v, gamma, eps, cos, sin, slots, k_cache, v_
     # gamma applied after the rotation instead of before it
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
-    kn = orc.rms_norm(k, np.ones_like(gamma), eps)
-    kr = orc.rotate_tokens(kn, cos, sin) * np.asarray(gamma)
+    kn = k if gamma is None else orc.rms_norm(k, np.ones_like(gamma), eps)
+    kr = orc.rotate_tokens(kn, cos, sin) * (1.0 if gamma is None else np.asarray(gamma))
     for t, slot in enumerate(np.asarray(slots).tolist()):
-        if slot >= 0:
+        if 0 <= slot < kc.shape[0]:
             kc[slot] = kr[t]
             vc[slot] = v[t]
     return kc, vc
