@@ -12,8 +12,8 @@ The value is TFLOP/s of causal attention (4*B*Hq*S^2*D/2 per step) over the time
 steps.  The roofline object reports the attention kernel's own time, measured with HIP
 events on the stream it runs on, against the dense bf16 MFMA peak.  Extra measurements
 (after the timed region): rope_tables GB/s at the op's size limits, rope_qk GB/s on the
-workload, and the unfused path (rope_qk + attention without rotation) for the fusion
-ablation.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
+workload, the unfused path (rope_qk + attention without rotation) for the fusion
+ablation, and the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
 """
 
 import argparse
@@ -269,6 +269,28 @@ def main():
                 comp[f"rope_tables_{dt_name}_T256000_D{Dt}_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
                 comp[f"rope_tables_{dt_name}_T256000_D{Dt}_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                 del ts, tc
+        torch.cuda.empty_cache()
+        # fused RMSNorm + RoPE + KV-cache write on a 16 x 4096-token prefill into a paged cache:
+        # reads K, V and the table rows, writes K', V into the cache (slots, gamma are small)
+        cw = wl.CACHE_CONFIGS["prefill"]
+        ci = wl.generate_cache(cw)
+        ck, cv = ci.k.to(dev), ci.v.to(dev)
+        kc, vc = ci.k_cache.to(dev), ci.v_cache.to(dev)
+        cgam, cslots = ci.gamma.to(dev), torch.from_numpy(ci.slots).to(dev)
+        clens = np.full(cw.batch, cw.new_tokens, dtype=np.int32)
+        cf = torch.from_numpy(rfa.inv_freq(cw.base, cw.head_dim, clens)).to(dev)
+        csin, ccos = rfa.rope_tables(torch.from_numpy(ci.pos).to(dev), cf, clens, cw.head_dim, 1.0, cw.torch_dtype)
+        fn = lambda: rfa.rope_kv_rms_norm_rope_cache(ck, cv, ccos, csin, cslots, kc, vc, gamma=cgam, eps=1e-6)
+        for _ in range(3):
+            fn()
+        ms = time_events(fn, 20, torch)
+        esz = ck.element_size()
+        cb = 4 * ck.numel() * esz + 2 * csin.numel() * esz + 8 * cslots.numel() + 4 * cgam.numel()
+        comp["kv_cache_workload"] = cw.name
+        comp["kv_cache_ms"] = round(ms, 4)
+        comp["kv_cache_gbps"] = round(cb / (ms * 1e-3) / 1e9, 1)
+        comp["kv_cache_hbm_frac"] = round(cb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del ck, cv, kc, vc, ci
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -1,7 +1,8 @@
 /*
  * rope_fa.h — C ABI of librope_fa.so: rotary position embedding (RoPE) tables,
- * the standalone rotate-half RoPE of Q and K, and RoPE fused into a causal
- * FlashAttention-style forward pass, for AMD Instinct MI355X (gfx950).
+ * the standalone rotate-half RoPE of Q and K, RoPE fused into a causal
+ * FlashAttention-style forward pass, and the fused RMSNorm + RoPE + KV-cache write,
+ * for AMD Instinct MI355X (gfx950).
  *
  * Page key for the citations below (the source pages of the method):
  *   [RoPE-fusion blog]     devpress.csdn.net/awstech/6a91ac403bda720d4b352e13
@@ -193,6 +194,68 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
  */
 rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream);
+
+/*
+ * Parameters of rope_kv_rms_norm_rope_cache.
+ *
+ * New tokens are rows t < ntokens of k and v: head h of token t lives at
+ * base + t*stride[0] + h*stride[1] + d (strides {token, head} in elements, dim stride 1).
+ *
+ * Cache addressing.  A cache slot s is split into block s / block_size and offset
+ * s % block_size; head h of slot s lives at
+ *   cache + (s / block_size)*c_stride[0] + (s % block_size)*c_stride[1] + h*c_stride[2] + d.
+ * block_size = the cache length of one sequence gives a contiguous per-sequence cache,
+ * [B, S_max, hkv, D] (c_stride {S_max*hkv*D, hkv*D, D}) or [B, hkv, S_max, D]
+ * (c_stride {hkv*S_max*D, D, S_max*D}); a smaller block_size gives a paged cache
+ * [num_blocks, block_size, hkv, D] (the paged KV-cache management the [FlashAttention
+ * blog] points to in its KV-cache pitfall).
+ */
+typedef struct rope_kv_cache_params {
+    uint32_t struct_size;       /* = sizeof(rope_kv_cache_params), else ROPE_ERR_ABI */
+    rope_dtype dtype;           /* k, v, cos, sin, k_cache, v_cache: F32 | F16 | BF16 */
+    const void* k;              /* DEVICE [ntokens, hkv, head_dim] by k_stride */
+    const void* v;              /* DEVICE [ntokens, hkv, head_dim] by v_stride; NULL together with
+                                   v_cache = K only.  k, v, cos, sin and slots may be NULL when
+                                   ntokens == 0 */
+    const float* gamma;         /* DEVICE float [head_dim] RMSNorm weight; NULL = no normalisation */
+    const void* cos;            /* DEVICE [ntokens, head_dim] of dtype: row t serves new token t */
+    const void* sin;
+    const int64_t* slots;       /* DEVICE int64 [ntokens]: cache slot of each new token; a slot < 0 or
+                                   >= num_blocks * block_size skips the token (nothing written) */
+    void* k_cache;              /* DEVICE, addressed by kc_stride as above */
+    void* v_cache;              /* DEVICE, addressed by vc_stride; NULL together with v */
+    int32_t ntokens;            /* new tokens, >= 0 (0: nothing is enqueued) */
+    int32_t hkv;                /* heads of k and v, >= 1 */
+    int32_t head_dim;           /* multiple of 32, <= ROPE_MAX_HEAD_SIZE */
+    int32_t block_size;         /* slots per cache block, >= 1 */
+    int32_t num_blocks;         /* cache blocks, >= 1 */
+    float eps;                  /* RMSNorm epsilon, finite and >= 0 */
+    int64_t k_stride[2];        /* {token, head} in elements */
+    int64_t v_stride[2];
+    int64_t kc_stride[3];       /* {block, offset in block, head} in elements */
+    int64_t vc_stride[3];
+    uint8_t rsv[16];            /* reserved, must be zero */
+} rope_kv_cache_params;
+
+/*
+ * rope_kv_rms_norm_rope_cache — the fused "RMSNorm, RoPE, write to the KV cache" step
+ * that precedes attention (kv_rms_norm_rope_cache, named in the [RoPE-fusion blog],
+ * section 五; the pages do not define it, this is the reading taken).  For every new
+ * token t with a valid slot s = slots[t] and every kv head h, with x = k[t, h] (length
+ * D = head_dim):
+ *   y = gamma * x / sqrt(mean(x^2) + eps)           ([RoPE/GQA tutorial], section 八;
+ *                                                     y = x when gamma == NULL)
+ *   k_cache[s, h] = y*cos[t] + rotate_half(y)*sin[t]  (the rope_qk formula, all D columns)
+ *   v_cache[s, h] = v[t, h]                           (bit-exact copy)
+ * computed in float32 and rounded once to nearest-even into dtype.  Two tokens with the
+ * same slot race (which one lands is unspecified).  k and v must not overlap the caches.
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch (none
+ * when ntokens == 0).
+ */
+rope_status rope_kv_rms_norm_rope_cache(const rope_kv_cache_params* p, void* hip_stream);
+
+/* sizeof(rope_kv_cache_params) as compiled into the library (for bindings to check). */
+uint32_t rope_kv_cache_params_size(void);
 
 /* Static text for a status code ("ROPE_OK", ...); never NULL. */
 const char* rope_status_str(rope_status s);

@@ -6,7 +6,7 @@ in the library's HIP kernels.  There is no fallback: if the library is missing o
 call is rejected, an exception is raised.
 
 Names follow the C ABI: ``inv_freq`` (rope_inv_freq), ``rope_tables``, ``rope_qk``,
-``rope_flash_attn_fwd``.
+``rope_flash_attn_fwd``, ``rope_kv_rms_norm_rope_cache``.
 """
 
 from __future__ import annotations
@@ -25,7 +25,9 @@ __all__ = [
     "rope_tables",
     "rope_qk",
     "rope_flash_attn_fwd",
+    "rope_kv_rms_norm_rope_cache",
     "RopeAttnParams",
+    "RopeKvCacheParams",
     "STATUS",
     "DTYPE",
     "LIB_PATH",
@@ -81,6 +83,34 @@ class RopeAttnParams(ctypes.Structure):
     ]
 
 
+class RopeKvCacheParams(ctypes.Structure):
+    """Mirror of ``rope_kv_cache_params`` in include/rope_fa.h (checked against the library's size)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p),
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("slots", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("ntokens", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("k_stride", ctypes.c_int64 * 2),
+        ("v_stride", ctypes.c_int64 * 2),
+        ("kc_stride", ctypes.c_int64 * 3),
+        ("vc_stride", ctypes.c_int64 * 3),
+        ("rsv", ctypes.c_uint8 * 16),
+    ]
+
+
 _lib = None
 
 
@@ -101,6 +131,9 @@ def lib() -> ctypes.CDLL:
     L.rope_qk.restype = st
     L.rope_flash_attn_fwd.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
     L.rope_flash_attn_fwd.restype = st
+    L.rope_kv_rms_norm_rope_cache.argtypes = [ctypes.POINTER(RopeKvCacheParams), vp]
+    L.rope_kv_rms_norm_rope_cache.restype = st
+    L.rope_kv_cache_params_size.restype = ctypes.c_uint32
     L.rope_status_str.argtypes = [ctypes.c_int]
     L.rope_status_str.restype = ctypes.c_char_p
     L.rope_abi_version.restype = i32
@@ -109,6 +142,8 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError("librope_fa ABI version mismatch")
     if L.rope_attn_params_size() != ctypes.sizeof(RopeAttnParams):
         raise RuntimeError("rope_attn_params layout mismatch between binding and library")
+    if L.rope_kv_cache_params_size() != ctypes.sizeof(RopeKvCacheParams):
+        raise RuntimeError("rope_kv_cache_params layout mismatch between binding and library")
     _lib = L
     return L
 
@@ -281,3 +316,66 @@ def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: 
         p.lse = lse.data_ptr()
     _check("rope_flash_attn_fwd", lib().rope_flash_attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------------------- rope_kv_rms_norm_rope_cache
+def _cache_strides(c: torch.Tensor, cache_layout: str):
+    """{block, offset in block, head} strides and (num_blocks, block_size, heads, head_dim)."""
+    if c.dim() != 4 or c.stride(3) != 1:
+        raise ValueError("caches must be 4-D with a unit head_dim stride")
+    if cache_layout == "BSND":   # [num_blocks, block_size, hkv, D]
+        return (c.stride(0), c.stride(1), c.stride(2)), (c.shape[0], c.shape[1], c.shape[2], c.shape[3])
+    if cache_layout == "BNSD":   # [num_blocks, hkv, block_size, D]
+        return (c.stride(0), c.stride(2), c.stride(1)), (c.shape[0], c.shape[2], c.shape[1], c.shape[3])
+    raise ValueError(f"unknown cache layout {cache_layout}")
+
+
+def rope_kv_rms_norm_rope_cache(k: torch.Tensor, v: Optional[torch.Tensor], cos: torch.Tensor, sin: torch.Tensor,
+                                slots: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], *,
+                                gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                cache_layout: str = "BSND"):
+    """RMSNorm (if gamma is given) + RoPE of k [T, hkv, D], written with v into the caches at ``slots``.
+
+    Caches are [num_blocks, block_size, hkv, D] ("BSND") or [num_blocks, hkv, block_size, D]
+    ("BNSD"); slot s is block s // block_size, offset s % block_size.  Updates the caches in
+    place and returns them.
+    """
+    _need_cuda(k, v, cos, sin, slots, k_cache, v_cache, gamma)
+    if (v is None) != (v_cache is None):
+        raise ValueError("v and v_cache go together")
+    if k.dim() != 3 or k.stride(2) != 1:
+        raise ValueError("k must be [ntokens, hkv, head_dim] with a unit head_dim stride")
+    T, H, D = k.shape
+    kcs, kshape = _cache_strides(k_cache, cache_layout)
+    if kshape[2:] != (H, D) or k_cache.dtype != k.dtype:
+        raise ValueError("k_cache must hold hkv heads of head_dim and k's dtype")
+    p = RopeKvCacheParams()
+    p.struct_size = ctypes.sizeof(RopeKvCacheParams)
+    p.dtype = DTYPE.get(k.dtype, -1)
+    p.k, p.k_cache = k.data_ptr(), k_cache.data_ptr()
+    p.k_stride[:] = (k.stride(0), k.stride(1))
+    p.kc_stride[:] = kcs
+    if v is not None:
+        vcs, vshape = _cache_strides(v_cache, cache_layout)
+        if v.shape != k.shape or v.stride(2) != 1 or v.dtype != k.dtype or vshape != kshape \
+                or v_cache.dtype != k.dtype:
+            raise ValueError("v and v_cache must match k and k_cache")
+        p.v, p.v_cache = v.data_ptr(), v_cache.data_ptr()
+        p.v_stride[:] = (v.stride(0), v.stride(1))
+        p.vc_stride[:] = vcs
+    for t in (cos, sin):
+        if t.dtype != k.dtype or not t.is_contiguous() or t.dim() != 2 or t.shape[1] != D or t.shape[0] < T:
+            raise ValueError("tables must be contiguous [>= ntokens, head_dim] of k's dtype")
+    p.cos, p.sin = cos.data_ptr(), sin.data_ptr()
+    if slots.dtype != torch.int64 or not slots.is_contiguous() or slots.numel() != T:
+        raise ValueError("slots must be contiguous int64 [ntokens]")
+    p.slots = slots.data_ptr()
+    if gamma is not None:
+        if gamma.dtype != torch.float32 or not gamma.is_contiguous() or gamma.numel() != D:
+            raise ValueError("gamma must be contiguous float32 [head_dim]")
+        p.gamma = gamma.data_ptr()
+    p.ntokens, p.hkv, p.head_dim = T, H, D
+    p.num_blocks, p.block_size = kshape[0], kshape[1]
+    p.eps = float(eps)
+    _check("rope_kv_rms_norm_rope_cache", lib().rope_kv_rms_norm_rope_cache(ctypes.byref(p), _stream(k)))
+    return k_cache, v_cache

@@ -20,6 +20,7 @@ hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const i
                               void* sin_out, void* cos_out, hipStream_t stream);
 hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
+hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream);
 }  // namespace ropefa
 
 using ropefa::dtype_bytes;
@@ -98,6 +99,47 @@ rope_status check_params(const rope_attn_params* p, bool attention) {
     return ROPE_OK;
 }
 
+rope_status check_kv_cache(const rope_kv_cache_params* p) {
+    if (!p) return ROPE_ERR_NULL;
+    if (p->struct_size != sizeof(rope_kv_cache_params)) return ROPE_ERR_ABI;
+    for (unsigned char c : p->rsv)
+        if (c) return ROPE_ERR_ABI;
+    if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
+    if (p->ntokens < 0 || p->hkv <= 0 || p->head_dim <= 0) return ROPE_ERR_SHAPE;
+    // the new tokens' arrays may be NULL when there are none (empty allocations)
+    if (p->ntokens > 0 && (!p->k || !p->cos || !p->sin || !p->slots)) return ROPE_ERR_NULL;
+    if (!p->k_cache) return ROPE_ERR_NULL;
+    if (p->ntokens > 0 && (p->v == nullptr) != (p->v_cache == nullptr)) return ROPE_ERR_NULL;
+    if (p->block_size <= 0 || p->num_blocks <= 0) return ROPE_ERR_SHAPE;
+    if (p->head_dim % 32 != 0) return ROPE_ERR_UNSUPPORTED;
+    if (p->head_dim > ROPE_MAX_HEAD_SIZE) return ROPE_ERR_LIMIT;
+    if ((int64_t)p->ntokens * p->hkv > INT32_MAX) return ROPE_ERR_LIMIT;
+    if (!(std::isfinite(p->eps) && p->eps >= 0.0f)) return ROPE_ERR_SHAPE;
+    const int eb = dtype_bytes(p->dtype);
+    const int64_t* strides[2] = {p->k_stride, p->v_stride};
+    for (int i = 0; i < 2; ++i) {
+        if (i == 1 && !p->v_cache) continue;
+        for (int j = 0; j < 2; ++j) {
+            if (strides[i][j] < 0) return ROPE_ERR_SHAPE;
+            if ((strides[i][j] * eb) % 16 != 0) return ROPE_ERR_UNSUPPORTED;
+        }
+    }
+    const int64_t* cstrides[2] = {p->kc_stride, p->vc_stride};
+    for (int i = 0; i < 2; ++i) {
+        if (i == 1 && !p->v_cache) continue;
+        for (int j = 0; j < 3; ++j) {
+            if (cstrides[i][j] < 0) return ROPE_ERR_SHAPE;
+            if ((cstrides[i][j] * eb) % 16 != 0) return ROPE_ERR_UNSUPPORTED;
+        }
+    }
+    if (!aligned16(p->k) || !aligned16(p->cos) || !aligned16(p->sin) || !aligned16(p->k_cache))
+        return ROPE_ERR_UNSUPPORTED;
+    if (!aligned16(p->v) || !aligned16(p->v_cache)) return ROPE_ERR_UNSUPPORTED;
+    if (p->gamma && !aligned16(p->gamma)) return ROPE_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(p->slots) & 7u) return ROPE_ERR_UNSUPPORTED;
+    return ROPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +161,8 @@ const char* rope_status_str(rope_status s) {
 int32_t rope_abi_version(void) { return ROPE_FA_ABI_VERSION; }
 
 uint32_t rope_attn_params_size(void) { return (uint32_t)sizeof(rope_attn_params); }
+
+uint32_t rope_kv_cache_params_size(void) { return (uint32_t)sizeof(rope_kv_cache_params); }
 
 rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_lens, int32_t batch, int32_t trained_len,
                           float* out) {
@@ -175,6 +219,14 @@ rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream) {
     const rope_status st = check_params(p, true);
     if (st != ROPE_OK) return st;
     const hipError_t e = ropefa::launch_flash_fwd(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_kv_rms_norm_rope_cache(const rope_kv_cache_params* p, void* hip_stream) {
+    const rope_status st = check_kv_cache(p);
+    if (st != ROPE_OK) return st;
+    if (p->ntokens == 0) return ROPE_OK;
+    const hipError_t e = ropefa::launch_kv_cache(p, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 

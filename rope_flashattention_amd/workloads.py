@@ -9,6 +9,12 @@ drawn first as integers in [lo, hi] inclusive; then Q, K, V ~ N(0, 1) in float32
 that order, rounded to the workload dtype by torch's CPU cast (round to nearest even).
 Dense tensors are BNSD [batch, heads, seq, head_dim]; varlen tensors are packed
 [ntokens, heads, head_dim].  Positions are 0 .. L-1 for every sequence.
+
+KV-cache workloads (``CacheWorkload``): context lengths already in the cache are drawn
+first as integers in [lo, hi] inclusive, then a shuffled block table (a random
+permutation of the cache blocks, as a paged allocator would hand them out), then the
+new tokens' K, V ~ N(0, 1), the RMSNorm weight gamma ~ U[0.5, 2) in float32, and the
+previous cache contents ~ N(0, 1), in that order.
 """
 
 from __future__ import annotations
@@ -126,3 +132,75 @@ def causal_flops(w: Workload, seq_lens) -> float:
     per = sum(float(L) * float(L) for L in np.asarray(seq_lens).tolist())
     f = 4.0 * w.hq * per * w.head_dim
     return f / 2.0 if w.causal else f
+
+
+# --------------------------------------------------------------------------- KV-cache workloads
+@dataclasses.dataclass(frozen=True)
+class CacheWorkload:
+    name: str
+    dtype: str
+    batch: int
+    hkv: int
+    head_dim: int
+    new_tokens: int                 # new tokens per sequence (a prefill chunk; 1 = one decode step)
+    ctx_range: Tuple[int, int]      # tokens already cached per sequence, inclusive bounds
+    block_size: int                 # cache block (page) size in tokens
+    max_len: int                    # cache capacity per sequence, a multiple of block_size
+    hq: int = 0                     # query heads (decode attention)
+    base: float = 10000.0
+    seed: int = 0
+
+    @property
+    def torch_dtype(self):
+        return TORCH_DTYPES[self.dtype]
+
+    @property
+    def blocks_per_seq(self) -> int:
+        return self.max_len // self.block_size
+
+
+CACHE_CONFIGS = {
+    "prefill": CacheWorkload("kv-cache prefill 16 seqs x 4096 new, H8 D128 bf16, paged block 16", "bf16", 16, 8,
+                             128, new_tokens=4096, ctx_range=(0, 0), block_size=16, max_len=4096, seed=3001),
+    "small": CacheWorkload("small kv-cache 3 seqs x 37 new after U[0,100], H2 D128 bf16, block 16", "bf16", 3, 2,
+                           128, new_tokens=37, ctx_range=(0, 100), block_size=16, max_len=144, seed=3002),
+}
+
+
+@dataclasses.dataclass
+class CacheInputs:
+    workload: CacheWorkload
+    k: torch.Tensor              # CPU [T, hkv, D] workload dtype, T = batch * new_tokens
+    v: torch.Tensor
+    gamma: torch.Tensor          # CPU float32 [D]
+    k_cache: torch.Tensor        # CPU [num_blocks, block_size, hkv, D] previous contents
+    v_cache: torch.Tensor
+    ctx: np.ndarray              # int32 [batch] tokens already cached
+    pos: np.ndarray              # int32 [T] position of every new token
+    block_table: np.ndarray      # int64 [batch, blocks_per_seq] physical block of each logical block
+    slots: np.ndarray            # int64 [T] cache slot of every new token
+
+    @property
+    def ntokens(self) -> int:
+        return int(self.pos.size)
+
+
+def generate_cache(w: CacheWorkload, seed: Optional[int] = None) -> CacheInputs:
+    if w.max_len % w.block_size or w.ctx_range[1] + w.new_tokens > w.max_len:
+        raise ValueError("cache too small for the drawn lengths")
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    lo, hi = w.ctx_range
+    ctx = rng.integers(lo, hi + 1, size=w.batch).astype(np.int32)
+    nblocks = w.batch * w.blocks_per_seq
+    block_table = rng.permutation(nblocks).astype(np.int64).reshape(w.batch, w.blocks_per_seq)
+    T = w.batch * w.new_tokens
+    pos = np.concatenate([c + np.arange(w.new_tokens, dtype=np.int32) for c in ctx.tolist()])
+    seq = np.repeat(np.arange(w.batch), w.new_tokens)
+    slots = block_table[seq, pos // w.block_size] * w.block_size + pos % w.block_size
+    k = _normal(rng, (T, w.hkv, w.head_dim), w.torch_dtype)
+    v = _normal(rng, (T, w.hkv, w.head_dim), w.torch_dtype)
+    gamma = torch.from_numpy(rng.uniform(0.5, 2.0, size=w.head_dim).astype(np.float32))
+    cshape = (nblocks, w.block_size, w.hkv, w.head_dim)
+    k_cache = _normal(rng, cshape, w.torch_dtype)
+    v_cache = _normal(rng, cshape, w.torch_dtype)
+    return CacheInputs(w, k, v, gamma, k_cache, v_cache, ctx, pos, block_table, slots.astype(np.int64))

@@ -15,7 +15,7 @@ import pytest
 
 import oracle as orc
 import rope_flashattention_amd as rfa
-from rope_flashattention_amd import RopeAttnParams
+from rope_flashattention_amd import RopeAttnParams, RopeKvCacheParams
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rope_fa.h")
@@ -37,7 +37,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(ropelib):
     names = declared_functions()
-    assert {"rope_tables", "rope_qk", "rope_flash_attn_fwd", "rope_inv_freq"} <= set(names)
+    assert {"rope_tables", "rope_qk", "rope_flash_attn_fwd", "rope_inv_freq",
+            "rope_kv_rms_norm_rope_cache"} <= set(names)
     for n in names:
         assert hasattr(ropelib, n), n
 
@@ -45,6 +46,7 @@ def test_library_exports_every_declared_symbol(ropelib):
 def test_abi_version_and_struct_size(ropelib):
     assert ropelib.rope_abi_version() == 1
     assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
+    assert ropelib.rope_kv_cache_params_size() == ctypes.sizeof(RopeKvCacheParams)
     for s, name in rfa.STATUS.items():
         assert ropelib.rope_status_str(s).decode() == name
 
@@ -210,6 +212,67 @@ def test_rope_qk_rejects(ropelib, kw, status):
 def test_null_params(ropelib):
     assert ropelib.rope_qk(None, None) == ST["ROPE_ERR_NULL"]
     assert ropelib.rope_flash_attn_fwd(None, None) == ST["ROPE_ERR_NULL"]
+
+
+# --------------------------------------------------------------------------- KV-cache step validation
+def valid_cache_params(dtype=2, D=128, H=8, T=16, blocks=4, bs=64):
+    p = RopeKvCacheParams()
+    p.struct_size = ctypes.sizeof(RopeKvCacheParams)
+    p.dtype = dtype
+    p.k = p.v = p.gamma = p.cos = p.sin = p.slots = p.k_cache = p.v_cache = FAKE
+    p.ntokens, p.hkv, p.head_dim, p.block_size, p.num_blocks = T, H, D, bs, blocks
+    p.eps = 1e-6
+    p.k_stride[:] = p.v_stride[:] = (H * D, D)
+    p.kc_stride[:] = p.vc_stride[:] = (bs * H * D, H * D, D)
+    return p
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), "ROPE_ERR_ABI"),
+    (dict(rsv=1), "ROPE_ERR_ABI"),
+    (dict(dtype=0), "ROPE_ERR_DTYPE"),
+    (dict(k=None), "ROPE_ERR_NULL"),
+    (dict(cos=None), "ROPE_ERR_NULL"),
+    (dict(slots=None), "ROPE_ERR_NULL"),
+    (dict(k_cache=None), "ROPE_ERR_NULL"),
+    (dict(v=None), "ROPE_ERR_NULL"),                 # v without v_cache
+    (dict(v_cache=None), "ROPE_ERR_NULL"),
+    (dict(ntokens=-1), "ROPE_ERR_SHAPE"),
+    (dict(hkv=0), "ROPE_ERR_SHAPE"),
+    (dict(block_size=0), "ROPE_ERR_SHAPE"),
+    (dict(num_blocks=0), "ROPE_ERR_SHAPE"),
+    (dict(eps=-1e-6), "ROPE_ERR_SHAPE"),
+    (dict(eps=float("nan")), "ROPE_ERR_SHAPE"),
+    (dict(head_dim=48), "ROPE_ERR_UNSUPPORTED"),
+    (dict(head_dim=4096), "ROPE_ERR_LIMIT"),
+    (dict(ntokens=2**28, hkv=16), "ROPE_ERR_LIMIT"),
+    (dict(k_stride=(8 * 128, 127)), "ROPE_ERR_UNSUPPORTED"),
+    (dict(kc_stride=(64 * 8 * 128, 8 * 128, -128)), "ROPE_ERR_SHAPE"),
+    (dict(vc_stride=(64 * 8 * 128, 8 * 128 + 4, 128)), "ROPE_ERR_UNSUPPORTED"),
+    (dict(k=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
+    (dict(gamma=FAKE + 4), "ROPE_ERR_UNSUPPORTED"),
+    (dict(slots=FAKE + 4), "ROPE_ERR_UNSUPPORTED"),
+    (dict(v_cache=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
+])
+def test_kv_cache_rejects(ropelib, kw, status):
+    p = mutate(valid_cache_params(), **kw)
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == ST[status]
+
+
+@no_gpu_only
+def test_kv_cache_empty_and_null(ropelib):
+    assert ropelib.rope_kv_rms_norm_rope_cache(None, None) == ST["ROPE_ERR_NULL"]
+    # no new tokens: accepted, nothing enqueued
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(valid_cache_params(T=0)), None) == 0
+    # K only (v and v_cache both NULL) passes validation too: checked here with no tokens
+    p = mutate(valid_cache_params(T=0), v=None, v_cache=None)
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == 0
+    # with no tokens the token arrays may be NULL (empty allocations); the cache may not
+    p = mutate(valid_cache_params(T=0), k=None, v=None, cos=None, sin=None, slots=None)
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == 0
+    p = mutate(valid_cache_params(T=0), k_cache=None)
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == ST["ROPE_ERR_NULL"]
 
 
 def test_binding_refuses_cpu_tensors(ropelib):
