@@ -10,9 +10,10 @@
 //
 // Thread mapping: a group of G lanes (G a power of two dividing the wavefront) owns one
 // (token, head) row; lane l owns the chunk pairs (c, c + D/2) with c = l + p*G, 8 columns
-// each, so every rotation pair lives in one thread.  The sum of squares is reduced across
-// the group with xor shuffles.  A whole group leaves together (row past the end, or a
-// skipped slot), so every shuffle partner is live.
+// each, so every rotation pair lives in one thread.  Every load of a thread is issued
+// before any arithmetic (more bytes in flight per lane), V is stored straight away, then
+// the sum of squares is reduced across the group with xor shuffles.  A whole group leaves
+// together (row past the end, or a skipped slot), so every shuffle partner is live.
 #include "common.h"
 
 namespace ropefa {
@@ -37,6 +38,22 @@ struct KvCacheArgs {
     int32_t group;           // lanes per row, power of two <= 64
 };
 
+// Streaming loads of K and V: each byte is read once, so they are marked nontemporal and
+// do not displace the table rows that the other heads of the token re-read.
+template <typename T>
+__device__ __forceinline__ Chunk8<T> load_stream(const T* p) {
+    Chunk8<T> c;
+    c.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return c;
+}
+template <>
+__device__ __forceinline__ Chunk8<float> load_stream<float>(const float* p) {
+    Chunk8<float> c;
+    c.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    c.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+    return c;
+}
+
 template <typename T, int NP>
 __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
     const int G = a.group;
@@ -55,22 +72,47 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
     const int half = D >> 1;
     const int nchunk = half >> 3;
     const T* krow = reinterpret_cast<const T*>(a.k) + t * a.ks[0] + h * a.ks[1];
+    const T* vrow = reinterpret_cast<const T*>(a.v) + t * a.vs[0] + h * a.vs[1];
     const T* crow = reinterpret_cast<const T*>(a.cos) + (int64_t)t * D;
     const T* srow = reinterpret_cast<const T*>(a.sin) + (int64_t)t * D;
     T* kdst = reinterpret_cast<T*>(a.kc) + blk * a.kcs[0] + off * a.kcs[1] + h * a.kcs[2];
+    T* vdst = reinterpret_cast<T*>(a.vc) + blk * a.vcs[0] + off * a.vcs[1] + h * a.vcs[2];
 
-    float x[NP][8], y[NP][8];
-    float ss = 0.0f;
+    Chunk8<T> kx[NP], ky[NP], vx[NP], vy[NP], cx[NP], cy[NP], sx[NP], sy[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int c = lane + p * G;
         if (c < nchunk) {
-            unpack<T>(load_chunk<T>(krow + c * 8), x[p]);
-            unpack<T>(load_chunk<T>(krow + c * 8 + half), y[p]);
+            kx[p] = load_stream<T>(krow + c * 8);
+            ky[p] = load_stream<T>(krow + c * 8 + half);
+            if (a.v) {
+                vx[p] = load_stream<T>(vrow + c * 8);
+                vy[p] = load_stream<T>(vrow + c * 8 + half);
+            }
+            cx[p] = load_chunk<T>(crow + c * 8);
+            sx[p] = load_chunk<T>(srow + c * 8);
+            cy[p] = load_chunk<T>(crow + c * 8 + half);
+            sy[p] = load_chunk<T>(srow + c * 8 + half);
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[p][e] = y[p][e] = 0.0f;
+            kx[p] = ky[p] = zero_chunk<T>();
         }
+    }
+    if (a.v) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int c = lane + p * G;
+            if (c < nchunk) {
+                store_chunk<T>(vdst + c * 8, vx[p]);
+                store_chunk<T>(vdst + c * 8 + half, vy[p]);
+            }
+        }
+    }
+    float x[NP][8], y[NP][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        unpack<T>(kx[p], x[p]);
+        unpack<T>(ky[p], y[p]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += x[p][e] * x[p][e] + y[p][e] * y[p][e];
     }
@@ -96,27 +138,14 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
     for (int p = 0; p < NP; ++p) {
         const int c = lane + p * G;
         if (c < nchunk) {
-            const int j = c * 8;
             float c0[8], s0[8], c1[8], s1[8];
-            unpack<T>(load_chunk<T>(crow + j), c0);
-            unpack<T>(load_chunk<T>(srow + j), s0);
-            unpack<T>(load_chunk<T>(crow + j + half), c1);
-            unpack<T>(load_chunk<T>(srow + j + half), s1);
+            unpack<T>(cx[p], c0);
+            unpack<T>(sx[p], s0);
+            unpack<T>(cy[p], c1);
+            unpack<T>(sy[p], s1);
             rotate_pair(x[p], y[p], c0, s0, c1, s1);
-            store_chunk<T>(kdst + j, pack<T>(x[p]));
-            store_chunk<T>(kdst + j + half, pack<T>(y[p]));
-        }
-    }
-    if (a.v) {
-        const T* vrow = reinterpret_cast<const T*>(a.v) + t * a.vs[0] + h * a.vs[1];
-        T* vdst = reinterpret_cast<T*>(a.vc) + blk * a.vcs[0] + off * a.vcs[1] + h * a.vcs[2];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int c = lane + p * G;
-            if (c < nchunk) {
-                store_chunk<T>(vdst + c * 8, load_chunk<T>(vrow + c * 8));
-                store_chunk<T>(vdst + c * 8 + half, load_chunk<T>(vrow + c * 8 + half));
-            }
+            store_chunk<T>(kdst + c * 8, pack<T>(x[p]));
+            store_chunk<T>(kdst + c * 8 + half, pack<T>(y[p]));
         }
     }
 }
