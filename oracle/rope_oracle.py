@@ -53,6 +53,8 @@ __all__ = [
     "DTYPE_FORMATS",
     "rms_norm",
     "kv_rms_norm_rope_cache",
+    "cache_slots",
+    "decode_attention",
 ]
 
 # (precision p incl. the implicit bit, minimum normal exponent emin)
@@ -359,6 +361,48 @@ def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
         kc[slot] = kr[t]
         vc[slot] = np.asarray(v[t], dtype=np.float64)
     return kc, vc
+
+
+def cache_slots(block_table_row, length: int, block_size: int) -> np.ndarray:
+    """Cache slots of logical token positions 0..length-1 of one sequence.
+
+    Token j lives in logical block j // block_size at offset j % block_size; the block
+    table maps the logical block to a physical one (paged KV cache, [FlashAttention blog],
+    KV-cache pitfall), so the slot is table[j // block_size] * block_size + j % block_size.
+    """
+    j = np.arange(int(length), dtype=np.int64)
+    table = np.asarray(block_table_row, dtype=np.int64)
+    return table[j // block_size] * block_size + j % block_size
+
+
+def decode_attention(q, cos, sin, k_cache, v_cache, block_table, cache_lens, block_size: int, scale: float):
+    """One decode step: each sequence's new query attends to every token in its cache.
+
+    The query q[b, h] (one new token per sequence) is rotated with its table row
+    (cos[b], sin[b]; the Rope-op matrix of ``rope_op_matrix``); the cached keys are used as
+    stored (they were rotated when written, see ``kv_rms_norm_rope_cache``).  For q head h
+    and kv head h // (Hq / Hkv) ([RoPE/GQA tutorial], sections 十一/十二):
+      out[b, h] = softmax_j(scale * q'[b, h] . K[b, j]) @ V[b, j],  j < cache_lens[b]
+    ([FlashAttention blog]: Softmax(QK^T / sqrt(d)) V).  All keys of the cache precede the
+    query, so nothing is masked.  q: [B, Hq, D]; cos, sin: [B, D]; caches: [num_slots, Hkv, D];
+    block_table: [B, max_blocks].  Returns (out [B, Hq, D], lse [B, Hq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = kc.shape[1]
+    g = Hq // Hkv
+    qr = rotate_tokens(q, cos, sin)
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        sl = cache_slots(block_table[b], int(cache_lens[b]), block_size)
+        K, V = kc[sl], vc[sl]                       # [L, Hkv, D]
+        for h in range(Hq):
+            o, l = attention(qr[b, h][None, :], K[:, h // g], V[:, h // g], scale, causal=False)
+            out[b, h], lse[b, h] = o[0], l[0]
+    return out, lse
 
 
 # --------------------------------------------------------------------------- numerics helpers

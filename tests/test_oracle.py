@@ -405,6 +405,87 @@ def test_kv_rms_norm_rope_cache():
     check_kv_cache(orc.kv_rms_norm_rope_cache)
 
 
+# --------------------------------------------------------------------------- decode over a paged cache
+def check_cache_slots(cache_slots):
+    # hand-worked: blocks of 4, logical blocks 0, 1 -> physical 5, 2
+    assert cache_slots([5, 2], 6, 4).tolist() == [20, 21, 22, 23, 8, 9]
+    assert cache_slots([3], 0, 4).tolist() == []
+    assert cache_slots([7, 1, 4], 9, 3).tolist() == [21, 22, 23, 3, 4, 5, 12, 13, 14]
+
+
+def test_cache_slots():
+    check_cache_slots(orc.cache_slots)
+
+
+def _decode_brute(q, cos, sin, kc, vc, table, lens, bs, scale):
+    """Scalar loops: rotate the query pair by pair, then exp-weighted sums over the cache."""
+    B, Hq, D = q.shape
+    Hkv = kc.shape[1]
+    h2 = D // 2
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            qr = [0.0] * D
+            for i in range(h2):
+                qr[i] = q[b, h, i] * cos[b, i] - q[b, h, i + h2] * sin[b, i]
+                qr[i + h2] = q[b, h, i + h2] * cos[b, i + h2] + q[b, h, i] * sin[b, i + h2]
+            kv = h // (Hq // Hkv)
+            scores = []
+            for j in range(lens[b]):
+                slot = table[b][j // bs] * bs + j % bs
+                scores.append(scale * sum(qr[d] * kc[slot, kv, d] for d in range(D)))
+            m = max(scores)
+            w = [math.exp(x - m) for x in scores]
+            tot = sum(w)
+            for j in range(lens[b]):
+                slot = table[b][j // bs] * bs + j % bs
+                for d in range(D):
+                    out[b, h, d] += w[j] / tot * vc[slot, kv, d]
+            lse[b, h] = m + math.log(tot)
+    return out, lse
+
+
+def check_decode(decode_attention, cache_slots):
+    r = rng(10)
+    # brute force on a tiny paged cache with GQA and two lengths
+    B, Hq, Hkv, D, bs = 2, 4, 2, 8, 2
+    lens = [3, 5]
+    table = [[4, 0, 7], [1, 6, 3]]
+    kc = r.standard_normal((16, Hkv, D))
+    vc = r.standard_normal((16, Hkv, D))
+    q = r.standard_normal((B, Hq, D))
+    cos = r.uniform(-1, 1, (B, D))
+    sin = r.uniform(-1, 1, (B, D))
+    o, l = decode_attention(q, cos, sin, kc, vc, table, lens, bs, 0.7)
+    ob, lb = _decode_brute(q, cos, sin, kc, vc, table, lens, bs, 0.7)
+    assert np.max(np.abs(o - ob)) < 1e-12 and np.max(np.abs(l - lb)) < 1e-12
+    # a single cached token: the output is its V, the lse its score
+    o1, l1 = decode_attention(q[:1], cos[:1], sin[:1], kc, vc, [[5]], [1], 3, 1.0)
+    assert np.max(np.abs(o1[0] - vc[15, np.arange(Hq) // 2])) < 1e-15
+    # the last row of causal prefill attention: cache built from the prefill's keys,
+    # written through a shuffled paged block table
+    L, Hq, Hkv, D, bs = 37, 4, 2, 16, 8
+    qs = r.standard_normal((L, Hq, D))
+    ks = r.standard_normal((L, Hkv, D))
+    vs = r.standard_normal((L, Hkv, D))
+    f = orc.inv_freq(1e4, D)[None, :]
+    sn, cs = orc.rope_tables(np.arange(L, dtype=np.int32), f, [L], 1.0)
+    nblk = 6
+    table = r.permutation(nblk)[None, :]
+    slots = cache_slots(table[0], L, bs)
+    kc, vc = orc.kv_rms_norm_rope_cache(ks, vs, None, 0.0, cs, sn, slots, np.zeros((nblk * bs, Hkv, D)),
+                                        np.zeros((nblk * bs, Hkv, D)))
+    o, l = decode_attention(qs[L - 1:], cs[L - 1:], sn[L - 1:], kc, vc, table, [L], bs, 0.25)
+    po, pl = orc.rope_attention(qs, ks, vs, cs, sn, [L], 0.25, True)
+    assert np.max(np.abs(o[0] - po[L - 1])) < 1e-12
+    assert np.max(np.abs(l[0] - pl[:, L - 1])) < 1e-12
+
+
+def test_decode_attention():
+    check_decode(orc.decode_attention, orc.cache_slots)
+
+
 # --------------------------------------------------------------------------- planted mistakes
 # Each mutant is one plausible slip; at least one pin above must reject it.
 
@@ -496,6 +577,31 @@ def _mut_kv_cache_norm_after_rope(k, v, gamma, eps, cos, sin, slots, k_cache, v_
     return kc, vc
 
 
+def _mut_cache_slots_swapped(table_row, length, block_size):
+    j = np.arange(int(length), dtype=np.int64)
+    t = np.asarray(table_row, dtype=np.int64)
+    return t[(j % block_size) % t.size] * block_size + j // block_size
+
+
+def _mut_decode_gqa_modulo(q, cos, sin, k_cache, v_cache, block_table, cache_lens, block_size, scale):
+    B, Hq, D = np.asarray(q).shape
+    Hkv = np.asarray(k_cache).shape[1]
+    qr = orc.rotate_tokens(np.asarray(q, dtype=np.float64), cos, sin)
+    out, lse = np.zeros((B, Hq, D)), np.zeros((B, Hq))
+    for b in range(B):
+        sl = orc.cache_slots(block_table[b], int(cache_lens[b]), block_size)
+        for h in range(Hq):
+            o, l = orc.attention(qr[b, h][None], np.asarray(k_cache)[sl][:, h % Hkv],
+                                 np.asarray(v_cache)[sl][:, h % Hkv], scale, causal=False)
+            out[b, h], lse[b, h] = o[0], l[0]
+    return out, lse
+
+
+def _mut_decode_drops_last(q, cos, sin, k_cache, v_cache, block_table, cache_lens, block_size, scale):
+    lens = [max(1, int(x) - 1) for x in cache_lens]
+    return orc.decode_attention(q, cos, sin, k_cache, v_cache, block_table, lens, block_size, scale)
+
+
 def _mut_rope_attention_gqa_strided(q, k, v, cos, sin, seq_lens, scale, causal=True):
     hq, hkv = q.shape[1], k.shape[1]
     idx = np.arange(hq) % hkv                      # strided instead of contiguous groups
@@ -524,6 +630,10 @@ def _mut_rope_attention_no_segments(q, k, v, cos, sin, seq_lens, scale, causal=T
     ("segments ignored", lambda g: check_rope_attention(_mut_rope_attention_no_segments, orc.rope_attention_rows)),
     ("RMS without the mean", lambda g: check_rms_norm(_mut_rms_norm_no_mean)),
     ("gamma after the rotation", lambda g: check_kv_cache(_mut_kv_cache_norm_after_rope)),
+    ("block and offset swapped", lambda g: check_cache_slots(_mut_cache_slots_swapped)),
+    ("decode block and offset swapped", lambda g: check_decode(orc.decode_attention, _mut_cache_slots_swapped)),
+    ("decode GQA by modulo", lambda g: check_decode(_mut_decode_gqa_modulo, orc.cache_slots)),
+    ("decode drops the newest key", lambda g: check_decode(_mut_decode_drops_last, orc.cache_slots)),
 ])
 def test_pins_reject_planted_mistakes(name, run, golden_dir):
     with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
