@@ -13,7 +13,8 @@ steps.  The roofline object reports the attention kernel's own time, measured wi
 events on the stream it runs on, against the dense bf16 MFMA peak.  Extra measurements
 (after the timed region): rope_tables GB/s at the op's size limits, rope_qk GB/s on the
 workload, the unfused path (rope_qk + attention without rotation) for the fusion
-ablation, and the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
+ablation, the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill, and
+decode-step attention GB/s over a paged cache.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
 """
 
 import argparse
@@ -291,6 +292,32 @@ def main():
         comp["kv_cache_gbps"] = round(cb / (ms * 1e-3) / 1e9, 1)
         comp["kv_cache_hbm_frac"] = round(cb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         del ck, cv, kc, vc, ci
+        torch.cuda.empty_cache()
+        # decode step over a paged cache: 32 sequences with 1024..8192 cached tokens, Hq 64 / Hkv 8;
+        # both launches (split partials and their merge) inside the timed call
+        dw = wl.CACHE_CONFIGS["decode"]
+        di = wl.generate_cache(dw)
+        dlens = (di.ctx + 1).astype(np.int32)
+        dq = di.q.to(dev)
+        dkc, dvc = di.k_cache.to(dev), di.v_cache.to(dev)
+        dbt = torch.from_numpy(di.block_table.astype(np.int32)).to(dev)
+        dsl = torch.from_numpy(dlens).to(dev)
+        dfr = torch.from_numpy(rfa.inv_freq(dw.base, dw.head_dim)).to(dev)
+        dsin, dcos = rfa.rope_tables(torch.from_numpy(di.pos).to(dev), dfr, [dw.batch], dw.head_dim, 1.0,
+                                     dw.torch_dtype)
+        dkw = dict(max_seqlen=int(dlens.max()), block_table=dbt)
+        dws = torch.empty(rfa.decode_workspace_size(dq, dkc, dvc, dsl, **dkw), dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(dq)
+        fn = lambda: rfa.rope_decode_attn_fwd(dq, dkc, dvc, dsl, dcos, dsin, out=dout, workspace=dws, **dkw)
+        for _ in range(3):
+            fn()
+        ms = time_events(fn, 20, torch)
+        db = wl.decode_bytes(dw, dlens)
+        comp["decode_workload"] = dw.name
+        comp["decode_ms"] = round(ms, 4)
+        comp["decode_gbps"] = round(db / (ms * 1e-3) / 1e9, 1)
+        comp["decode_hbm_frac"] = round(db / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del dq, dkc, dvc, dws, di
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -1,8 +1,8 @@
 /*
  * rope_fa.h — C ABI of librope_fa.so: rotary position embedding (RoPE) tables,
  * the standalone rotate-half RoPE of Q and K, RoPE fused into a causal
- * FlashAttention-style forward pass, and the fused RMSNorm + RoPE + KV-cache write,
- * for AMD Instinct MI355X (gfx950).
+ * FlashAttention-style forward pass, the fused RMSNorm + RoPE + KV-cache write and
+ * decode-step RoPE + GQA attention over that cache, for AMD Instinct MI355X (gfx950).
  *
  * Page key for the citations below (the source pages of the method):
  *   [RoPE-fusion blog]     devpress.csdn.net/awstech/6a91ac403bda720d4b352e13
@@ -12,8 +12,9 @@
  *
  * Conventions shared by every entry point:
  *  - Plain C types only; no exception crosses this boundary.
- *  - The caller owns every buffer.  The library allocates no device or host
- *    memory and keeps no mutable global state; entry points are re-entrant.
+ *  - The caller owns every buffer, scratch space included (rope_decode_attn_fwd takes a
+ *    workspace).  The library allocates no device or host memory and keeps no mutable
+ *    global state; entry points are re-entrant.
  *  - Device work is enqueued on the caller's HIP stream (`hip_stream`, a
  *    hipStream_t passed as void*, NULL = the default stream) and is
  *    asynchronous: nothing here synchronizes the device.
@@ -45,7 +46,8 @@ typedef enum rope_status {
     ROPE_ERR_LIMIT = 4,        /* a documented size limit is exceeded */
     ROPE_ERR_UNSUPPORTED = 5,  /* well-formed but not served by the kernels (head_dim, stride, alignment) */
     ROPE_ERR_ABI = 6,          /* struct_size mismatch or reserved bytes not zero */
-    ROPE_ERR_HIP = 7           /* the HIP runtime reported an error for a launch */
+    ROPE_ERR_HIP = 7,          /* the HIP runtime reported an error for a launch */
+    ROPE_ERR_WORKSPACE = 8     /* the caller's workspace is missing, misaligned or too small */
 } rope_status;
 
 /* Element types.  UNDEFINED is never valid ([DynamicNTKOperation], 参数列表:
@@ -256,6 +258,78 @@ rope_status rope_kv_rms_norm_rope_cache(const rope_kv_cache_params* p, void* hip
 
 /* sizeof(rope_kv_cache_params) as compiled into the library (for bindings to check). */
 uint32_t rope_kv_cache_params_size(void);
+
+/*
+ * Parameters of rope_decode_attn_fwd: one decode step over a (paged) KV cache.
+ *
+ * Sequence b has cache_seqlens[b] tokens in the cache (the new token included, its K' and
+ * V already written, e.g. by rope_kv_rms_norm_rope_cache).  Its token j lives in logical
+ * block j / block_size at offset j % block_size; the physical block is
+ * block_table[b * max_blocks_per_seq + j / block_size], or b * max_blocks_per_seq +
+ * j / block_size when block_table is NULL (a contiguous per-sequence cache).  Head h of a
+ * physical slot is addressed as in rope_kv_cache_params (kc_stride, vc_stride).
+ */
+typedef struct rope_decode_params {
+    uint32_t struct_size;         /* = sizeof(rope_decode_params), else ROPE_ERR_ABI */
+    rope_dtype dtype;             /* q, cos, sin, k_cache, v_cache, out: F16 | BF16 */
+    const void* q;                /* DEVICE [batch, hq, head_dim] by q_stride: the new queries, not rotated */
+    const void* cos;              /* DEVICE [batch, head_dim] of dtype: row b rotates sequence b's query
+                                     (the table row of its position); NULL with sin = no rotation */
+    const void* sin;
+    const void* k_cache;          /* DEVICE, keys as stored (already rotated) */
+    const void* v_cache;          /* DEVICE */
+    const int32_t* block_table;   /* DEVICE int32 [batch, max_blocks_per_seq], or NULL (see above) */
+    const int32_t* cache_seqlens; /* DEVICE int32 [batch]: cached tokens per sequence */
+    void* out;                    /* DEVICE [batch, hq, head_dim] by o_stride */
+    float* lse;                   /* DEVICE float [batch, hq] natural-log sum of exp of the scaled
+                                     scores, or NULL */
+    void* workspace;              /* DEVICE scratch, 256-byte aligned, >= rope_decode_workspace_size() */
+    uint64_t workspace_bytes;     /* size of workspace in bytes */
+    int32_t batch;                /* sequences, 1..65535 */
+    int32_t hq, hkv;              /* query heads and cached kv heads, hq % hkv == 0 */
+    int32_t head_dim;             /* 64 or 128 */
+    int32_t block_size;           /* cache slots per block, >= 1 */
+    int32_t max_blocks_per_seq;   /* block-table row length, >= 1 */
+    int32_t num_blocks;           /* physical cache blocks, >= 1 */
+    int32_t max_seqlen;           /* HOST bound of cache_seqlens, 1..max_blocks_per_seq*block_size */
+    int32_t num_splits;           /* key-range splits per sequence: 0 = the library's choice, else 1..256 */
+    float softmax_scale;          /* multiplies q.k before the softmax */
+    int64_t q_stride[2];          /* {batch, head} in elements; head_dim stride 1 */
+    int64_t o_stride[2];
+    int64_t kc_stride[3];         /* {block, offset in block, head} in elements */
+    int64_t vc_stride[3];
+    uint8_t rsv[16];              /* reserved, must be zero */
+} rope_decode_params;
+
+/*
+ * rope_decode_workspace_size — bytes of workspace rope_decode_attn_fwd needs for these
+ * parameters (batch, hq, head_dim, hkv, max_seqlen, num_splits are read), or 0 when they
+ * are invalid.  Host only.
+ */
+uint64_t rope_decode_workspace_size(const rope_decode_params* p);
+
+/*
+ * rope_decode_attn_fwd — decode-step RoPE + GQA attention over a KV cache (the step after
+ * prefill whose memory traffic GQA exists to cut: [RoPE/GQA tutorial], sections 十一-十二,
+ * the KV cache shrinks by Hq/Hkv; the paged cache of the [FlashAttention blog]'s KV-cache
+ * pitfall).  For every sequence b and q head h, with g = hq / hkv and L = cache_seqlens[b]:
+ *   q' = rope(q[b, h]) with the table row b (the rope_qk formula; no rotation when cos and
+ *        sin are NULL)
+ *   out[b, h] = sum_{j < L} softmax_j(softmax_scale * q'.K[b, j, h / g]) V[b, j, h / g]
+ * with K, V read from the cache as stored.  Every kv head's cache is read once for its g
+ * query heads.  The key range of each sequence is split over num_splits partial passes
+ * that a second kernel merges (both on hip_stream; the workspace holds the partial
+ * results and must not be shared by calls that overlap).  Device-side values are trusted
+ * as follows: a length above max_seqlen is clamped to it; a length <= 0 gives a zero
+ * output and lse = -inf; block-table entries must lie in [0, num_blocks) (others are
+ * clamped into range, so the cache is never read out of bounds, but the result is then
+ * meaningless).  float32 accumulation; the output is rounded once to dtype.
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, WORKSPACE, HIP.  Two kernel launches.
+ */
+rope_status rope_decode_attn_fwd(const rope_decode_params* p, void* hip_stream);
+
+/* sizeof(rope_decode_params) as compiled into the library (for bindings to check). */
+uint32_t rope_decode_params_size(void);
 
 /* Static text for a status code ("ROPE_OK", ...); never NULL. */
 const char* rope_status_str(rope_status s);

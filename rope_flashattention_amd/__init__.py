@@ -6,7 +6,7 @@ in the library's HIP kernels.  There is no fallback: if the library is missing o
 call is rejected, an exception is raised.
 
 Names follow the C ABI: ``inv_freq`` (rope_inv_freq), ``rope_tables``, ``rope_qk``,
-``rope_flash_attn_fwd``, ``rope_kv_rms_norm_rope_cache``.
+``rope_flash_attn_fwd``, ``rope_kv_rms_norm_rope_cache``, ``rope_decode_attn_fwd``.
 """
 
 from __future__ import annotations
@@ -26,8 +26,11 @@ __all__ = [
     "rope_qk",
     "rope_flash_attn_fwd",
     "rope_kv_rms_norm_rope_cache",
+    "rope_decode_attn_fwd",
+    "decode_workspace_size",
     "RopeAttnParams",
     "RopeKvCacheParams",
+    "RopeDecodeParams",
     "STATUS",
     "DTYPE",
     "LIB_PATH",
@@ -36,7 +39,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_fa.so")
 
 STATUS = {0: "ROPE_OK", 1: "ROPE_ERR_NULL", 2: "ROPE_ERR_SHAPE", 3: "ROPE_ERR_DTYPE", 4: "ROPE_ERR_LIMIT",
-          5: "ROPE_ERR_UNSUPPORTED", 6: "ROPE_ERR_ABI", 7: "ROPE_ERR_HIP"}
+          5: "ROPE_ERR_UNSUPPORTED", 6: "ROPE_ERR_ABI", 7: "ROPE_ERR_HIP", 8: "ROPE_ERR_WORKSPACE"}
 DTYPE = {None: 0, torch.float16: 1, torch.bfloat16: 2, torch.float32: 3}
 ABI_VERSION = 1
 
@@ -111,6 +114,41 @@ class RopeKvCacheParams(ctypes.Structure):
     ]
 
 
+class RopeDecodeParams(ctypes.Structure):
+    """Mirror of ``rope_decode_params`` in include/rope_fa.h (checked against the library's size)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p),
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("cache_seqlens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("batch", ctypes.c_int32),
+        ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("q_stride", ctypes.c_int64 * 2),
+        ("o_stride", ctypes.c_int64 * 2),
+        ("kc_stride", ctypes.c_int64 * 3),
+        ("vc_stride", ctypes.c_int64 * 3),
+        ("rsv", ctypes.c_uint8 * 16),
+    ]
+
+
 _lib = None
 
 
@@ -134,6 +172,11 @@ def lib() -> ctypes.CDLL:
     L.rope_kv_rms_norm_rope_cache.argtypes = [ctypes.POINTER(RopeKvCacheParams), vp]
     L.rope_kv_rms_norm_rope_cache.restype = st
     L.rope_kv_cache_params_size.restype = ctypes.c_uint32
+    L.rope_decode_attn_fwd.argtypes = [ctypes.POINTER(RopeDecodeParams), vp]
+    L.rope_decode_attn_fwd.restype = st
+    L.rope_decode_workspace_size.argtypes = [ctypes.POINTER(RopeDecodeParams)]
+    L.rope_decode_workspace_size.restype = ctypes.c_uint64
+    L.rope_decode_params_size.restype = ctypes.c_uint32
     L.rope_status_str.argtypes = [ctypes.c_int]
     L.rope_status_str.restype = ctypes.c_char_p
     L.rope_abi_version.restype = i32
@@ -144,6 +187,8 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError("rope_attn_params layout mismatch between binding and library")
     if L.rope_kv_cache_params_size() != ctypes.sizeof(RopeKvCacheParams):
         raise RuntimeError("rope_kv_cache_params layout mismatch between binding and library")
+    if L.rope_decode_params_size() != ctypes.sizeof(RopeDecodeParams):
+        raise RuntimeError("rope_decode_params layout mismatch between binding and library")
     _lib = L
     return L
 
@@ -379,3 +424,85 @@ def rope_kv_rms_norm_rope_cache(k: torch.Tensor, v: Optional[torch.Tensor], cos:
     p.eps = float(eps)
     _check("rope_kv_rms_norm_rope_cache", lib().rope_kv_rms_norm_rope_cache(ctypes.byref(p), _stream(k)))
     return k_cache, v_cache
+
+
+# --------------------------------------------------------------------------- rope_decode_attn_fwd
+def _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, max_seqlen, softmax_scale,
+                   cache_layout, num_splits):
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [batch, hq, head_dim] with a unit head_dim stride")
+    B, Hq, D = q.shape
+    kcs, kshape = _cache_strides(k_cache, cache_layout)
+    vcs, vshape = _cache_strides(v_cache, cache_layout)
+    if kshape != vshape or kshape[3] != D or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("k_cache and v_cache must match each other, q's head_dim and q's dtype")
+    nblk, bs, Hkv = kshape[0], kshape[1], kshape[2]
+    p = RopeDecodeParams()
+    p.struct_size = ctypes.sizeof(RopeDecodeParams)
+    p.dtype = DTYPE.get(q.dtype, -1)
+    p.q, p.k_cache, p.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_contiguous() or cache_seqlens.numel() != B:
+        raise ValueError("cache_seqlens must be contiguous int32 [batch]")
+    p.cache_seqlens = cache_seqlens.data_ptr()
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2 \
+                or block_table.shape[0] != B:
+            raise ValueError("block_table must be contiguous int32 [batch, max_blocks_per_seq]")
+        p.block_table = block_table.data_ptr()
+        p.max_blocks_per_seq = block_table.shape[1]
+    else:
+        p.max_blocks_per_seq = nblk // B
+    if cos is not None or sin is not None:
+        for t in (cos, sin):
+            if t is None or t.dtype != q.dtype or not t.is_contiguous() or tuple(t.shape) != (B, D):
+                raise ValueError("cos and sin go together, contiguous [batch, head_dim] of q's dtype")
+        p.cos, p.sin = cos.data_ptr(), sin.data_ptr()
+    p.batch, p.hq, p.hkv, p.head_dim = B, Hq, Hkv, D
+    p.block_size, p.num_blocks = bs, nblk
+    p.max_seqlen = int(max_seqlen)
+    p.num_splits = int(num_splits)
+    p.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / D ** 0.5)
+    p.q_stride[:] = (q.stride(0), q.stride(1))
+    p.kc_stride[:] = kcs
+    p.vc_stride[:] = vcs
+    return p
+
+
+def decode_workspace_size(q, k_cache, v_cache, cache_seqlens, *, max_seqlen: int, block_table=None,
+                          cache_layout: str = "BSND", num_splits: int = 0) -> int:
+    """Workspace bytes rope_decode_attn_fwd needs for these shapes (rope_decode_workspace_size)."""
+    p = _decode_params(q, k_cache, v_cache, cache_seqlens, None, None, block_table, max_seqlen, None,
+                       cache_layout, num_splits)
+    return int(lib().rope_decode_workspace_size(ctypes.byref(p)))
+
+
+def rope_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_seqlens: torch.Tensor,
+                         cos: Optional[torch.Tensor] = None, sin: Optional[torch.Tensor] = None, *,
+                         max_seqlen: int, block_table: Optional[torch.Tensor] = None,
+                         softmax_scale: Optional[float] = None, cache_layout: str = "BSND", num_splits: int = 0,
+                         return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Decode-step attention of q [batch, hq, D] (rotated with cos/sin [batch, D]) over the caches.
+
+    Caches as in ``rope_kv_rms_norm_rope_cache``; block_table int32 [batch, max_blocks] or None
+    (sequence b owns blocks b*max_blocks .. , max_blocks = num_blocks // batch).  The workspace
+    (a byte tensor) is allocated here when not given.
+    """
+    _need_cuda(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, out, workspace)
+    p = _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, max_seqlen, softmax_scale,
+                       cache_layout, num_splits)
+    need = int(lib().rope_decode_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(2) != 1:
+        raise ValueError("out must match q")
+    p.out = out.data_ptr()
+    p.o_stride[:] = (out.stride(0), out.stride(1))
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+        p.lse = lse.data_ptr()
+    _check("rope_decode_attn_fwd", lib().rope_decode_attn_fwd(ctypes.byref(p), _stream(q)))
+    return (out, lse) if return_lse else out

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librope_fa.so")
-SOURCES = ["api.cpp", "rope_tables.hip", "rope_qk.hip", "flash_fwd.hip", "kv_cache.hip"]
+SOURCES = ["api.cpp", "rope_tables.hip", "rope_qk.hip", "flash_fwd.hip", "kv_cache.hip", "decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

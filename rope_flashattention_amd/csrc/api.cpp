@@ -21,6 +21,9 @@ hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const i
 hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream);
+hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream);
+int decode_num_splits(const rope_decode_params* p);
+uint64_t decode_workspace_bytes(const rope_decode_params* p, int nsplit);
 }  // namespace ropefa
 
 using ropefa::dtype_bytes;
@@ -140,6 +143,59 @@ rope_status check_kv_cache(const rope_kv_cache_params* p) {
     return ROPE_OK;
 }
 
+// Shape checks of rope_decode_params that the workspace size depends on.
+rope_status check_decode_shape(const rope_decode_params* p) {
+    if (!p) return ROPE_ERR_NULL;
+    if (p->struct_size != sizeof(rope_decode_params)) return ROPE_ERR_ABI;
+    for (unsigned char c : p->rsv)
+        if (c) return ROPE_ERR_ABI;
+    if (p->batch <= 0 || p->hq <= 0 || p->hkv <= 0 || p->head_dim <= 0) return ROPE_ERR_SHAPE;
+    if (p->hq % p->hkv != 0) return ROPE_ERR_SHAPE;
+    if (p->block_size <= 0 || p->max_blocks_per_seq <= 0 || p->num_blocks <= 0) return ROPE_ERR_SHAPE;
+    if (p->max_seqlen <= 0 || (int64_t)p->max_seqlen > (int64_t)p->max_blocks_per_seq * p->block_size)
+        return ROPE_ERR_SHAPE;
+    if (p->num_splits < 0) return ROPE_ERR_SHAPE;
+    if (p->num_splits > 256 || p->batch > 65535) return ROPE_ERR_LIMIT;
+    const int g = p->hq / p->hkv;
+    if ((int64_t)p->hkv * ((g + 31) / 32) > 65535) return ROPE_ERR_LIMIT;
+    if ((int64_t)p->batch * p->max_blocks_per_seq > INT32_MAX) return ROPE_ERR_LIMIT;
+    if (p->head_dim != 64 && p->head_dim != 128) return ROPE_ERR_UNSUPPORTED;
+    return ROPE_OK;
+}
+
+rope_status check_decode(const rope_decode_params* p) {
+    rope_status st = check_decode_shape(p);
+    if (st != ROPE_OK) return st;
+    if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
+    if (p->dtype == ROPE_DT_F32) return ROPE_ERR_UNSUPPORTED;
+    if (!p->q || !p->k_cache || !p->v_cache || !p->cache_seqlens || !p->out) return ROPE_ERR_NULL;
+    if ((p->cos == nullptr) != (p->sin == nullptr)) return ROPE_ERR_NULL;
+    if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f)) return ROPE_ERR_SHAPE;
+    const int eb = dtype_bytes(p->dtype);
+    const int64_t* s2[2] = {p->q_stride, p->o_stride};
+    for (const int64_t* s : s2)
+        for (int j = 0; j < 2; ++j) {
+            if (s[j] < 0) return ROPE_ERR_SHAPE;
+            if ((s[j] * eb) % 16 != 0) return ROPE_ERR_UNSUPPORTED;
+        }
+    const int64_t* s3[2] = {p->kc_stride, p->vc_stride};
+    for (const int64_t* s : s3)
+        for (int j = 0; j < 3; ++j) {
+            if (s[j] < 0) return ROPE_ERR_SHAPE;
+            if ((s[j] * eb) % 16 != 0) return ROPE_ERR_UNSUPPORTED;
+        }
+    if (!aligned16(p->q) || !aligned16(p->out) || !aligned16(p->k_cache) || !aligned16(p->v_cache))
+        return ROPE_ERR_UNSUPPORTED;
+    if (!aligned16(p->cos) || !aligned16(p->sin)) return ROPE_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(p->block_table) & 3u) || (reinterpret_cast<uintptr_t>(p->cache_seqlens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(p->lse) & 3u))
+        return ROPE_ERR_UNSUPPORTED;
+    const uint64_t need = ropefa::decode_workspace_bytes(p, ropefa::decode_num_splits(p));
+    if (!p->workspace || (reinterpret_cast<uintptr_t>(p->workspace) & 255u) || p->workspace_bytes < need)
+        return ROPE_ERR_WORKSPACE;
+    return ROPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +210,7 @@ const char* rope_status_str(rope_status s) {
         case ROPE_ERR_UNSUPPORTED: return "ROPE_ERR_UNSUPPORTED";
         case ROPE_ERR_ABI: return "ROPE_ERR_ABI";
         case ROPE_ERR_HIP: return "ROPE_ERR_HIP";
+        case ROPE_ERR_WORKSPACE: return "ROPE_ERR_WORKSPACE";
     }
     return "ROPE_ERR_UNKNOWN";
 }
@@ -163,6 +220,13 @@ int32_t rope_abi_version(void) { return ROPE_FA_ABI_VERSION; }
 uint32_t rope_attn_params_size(void) { return (uint32_t)sizeof(rope_attn_params); }
 
 uint32_t rope_kv_cache_params_size(void) { return (uint32_t)sizeof(rope_kv_cache_params); }
+
+uint32_t rope_decode_params_size(void) { return (uint32_t)sizeof(rope_decode_params); }
+
+uint64_t rope_decode_workspace_size(const rope_decode_params* p) {
+    if (check_decode_shape(p) != ROPE_OK) return 0;
+    return ropefa::decode_workspace_bytes(p, ropefa::decode_num_splits(p));
+}
 
 rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_lens, int32_t batch, int32_t trained_len,
                           float* out) {
@@ -227,6 +291,13 @@ rope_status rope_kv_rms_norm_rope_cache(const rope_kv_cache_params* p, void* hip
     if (st != ROPE_OK) return st;
     if (p->ntokens == 0) return ROPE_OK;
     const hipError_t e = ropefa::launch_kv_cache(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_decode_attn_fwd(const rope_decode_params* p, void* hip_stream) {
+    const rope_status st = check_decode(p);
+    if (st != ROPE_OK) return st;
+    const hipError_t e = ropefa::launch_decode(p, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 

@@ -13,8 +13,9 @@ Dense tensors are BNSD [batch, heads, seq, head_dim]; varlen tensors are packed
 KV-cache workloads (``CacheWorkload``): context lengths already in the cache are drawn
 first as integers in [lo, hi] inclusive, then a shuffled block table (a random
 permutation of the cache blocks, as a paged allocator would hand them out), then the
-new tokens' K, V ~ N(0, 1), the RMSNorm weight gamma ~ U[0.5, 2) in float32, and the
-previous cache contents ~ N(0, 1), in that order.
+new tokens' K, V ~ N(0, 1), the RMSNorm weight gamma ~ U[0.5, 2) in float32, the
+previous cache contents ~ N(0, 1) and, for workloads with query heads, the new tokens'
+Q ~ N(0, 1), in that order.
 """
 
 from __future__ import annotations
@@ -164,6 +165,13 @@ CACHE_CONFIGS = {
                              128, new_tokens=4096, ctx_range=(0, 0), block_size=16, max_len=4096, seed=3001),
     "small": CacheWorkload("small kv-cache 3 seqs x 37 new after U[0,100], H2 D128 bf16, block 16", "bf16", 3, 2,
                            128, new_tokens=37, ctx_range=(0, 100), block_size=16, max_len=144, seed=3002),
+    # one decode step: 32 sequences with 1024..8192 cached tokens (the new one included),
+    # 64 query heads over 8 kv heads (the long-context GQA shape), paged blocks of 16
+    "decode": CacheWorkload("decode B32 Hq64/Hkv8 D128 bf16, cache U[1024,8192], paged block 16", "bf16", 32, 8,
+                            128, new_tokens=1, ctx_range=(1023, 8191), block_size=16, max_len=8192, hq=64,
+                            base=1e6, seed=3010),
+    "decode-small": CacheWorkload("small decode B5 Hq8/Hkv2 D128 bf16, cache U[1,300], block 16", "bf16", 5, 2, 128,
+                                  new_tokens=1, ctx_range=(0, 299), block_size=16, max_len=304, hq=8, seed=3011),
 }
 
 
@@ -179,6 +187,7 @@ class CacheInputs:
     pos: np.ndarray              # int32 [T] position of every new token
     block_table: np.ndarray      # int64 [batch, blocks_per_seq] physical block of each logical block
     slots: np.ndarray            # int64 [T] cache slot of every new token
+    q: Optional[torch.Tensor] = None   # CPU [T, hq, D] new queries (workloads with hq > 0)
 
     @property
     def ntokens(self) -> int:
@@ -203,4 +212,13 @@ def generate_cache(w: CacheWorkload, seed: Optional[int] = None) -> CacheInputs:
     cshape = (nblocks, w.block_size, w.hkv, w.head_dim)
     k_cache = _normal(rng, cshape, w.torch_dtype)
     v_cache = _normal(rng, cshape, w.torch_dtype)
-    return CacheInputs(w, k, v, gamma, k_cache, v_cache, ctx, pos, block_table, slots.astype(np.int64))
+    q = _normal(rng, (T, w.hq, w.head_dim), w.torch_dtype) if w.hq > 0 else None
+    return CacheInputs(w, k, v, gamma, k_cache, v_cache, ctx, pos, block_table, slots.astype(np.int64), q)
+
+
+def decode_bytes(w: CacheWorkload, cache_lens) -> float:
+    """Algorithmic HBM bytes of one decode step: every cached K and V row of every kv head
+    read once, plus the queries, their table rows and the outputs."""
+    e = TORCH_DTYPES[w.dtype].itemsize
+    kv = 2.0 * float(np.sum(cache_lens)) * w.hkv * w.head_dim * e
+    return kv + w.batch * (2 * w.hq * w.head_dim + 2 * w.head_dim) * e

@@ -15,7 +15,7 @@ import pytest
 
 import oracle as orc
 import rope_flashattention_amd as rfa
-from rope_flashattention_amd import RopeAttnParams, RopeKvCacheParams
+from rope_flashattention_amd import RopeAttnParams, RopeDecodeParams, RopeKvCacheParams
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rope_fa.h")
@@ -38,7 +38,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(ropelib):
     names = declared_functions()
     assert {"rope_tables", "rope_qk", "rope_flash_attn_fwd", "rope_inv_freq",
-            "rope_kv_rms_norm_rope_cache"} <= set(names)
+            "rope_kv_rms_norm_rope_cache", "rope_decode_attn_fwd", "rope_decode_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(ropelib, n), n
 
@@ -47,6 +47,7 @@ def test_abi_version_and_struct_size(ropelib):
     assert ropelib.rope_abi_version() == 1
     assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
     assert ropelib.rope_kv_cache_params_size() == ctypes.sizeof(RopeKvCacheParams)
+    assert ropelib.rope_decode_params_size() == ctypes.sizeof(RopeDecodeParams)
     for s, name in rfa.STATUS.items():
         assert ropelib.rope_status_str(s).decode() == name
 
@@ -273,6 +274,76 @@ def test_kv_cache_empty_and_null(ropelib):
     assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == 0
     p = mutate(valid_cache_params(T=0), k_cache=None)
     assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == ST["ROPE_ERR_NULL"]
+
+
+# --------------------------------------------------------------------------- decode validation
+def valid_decode_params(dtype=2, D=128, B=4, hq=16, hkv=4, bs=16, mb=64, L=1000, ws=None):
+    p = RopeDecodeParams()
+    p.struct_size = ctypes.sizeof(RopeDecodeParams)
+    p.dtype = dtype
+    p.q = p.cos = p.sin = p.k_cache = p.v_cache = p.block_table = p.cache_seqlens = p.out = FAKE
+    p.batch, p.hq, p.hkv, p.head_dim = B, hq, hkv, D
+    p.block_size, p.max_blocks_per_seq, p.num_blocks, p.max_seqlen = bs, mb, B * mb, L
+    p.softmax_scale = 1.0 / math.sqrt(D)
+    p.q_stride[:] = p.o_stride[:] = (hq * D, D)
+    p.kc_stride[:] = p.vc_stride[:] = (bs * hkv * D, hkv * D, D)
+    p.workspace = 0x100000
+    p.workspace_bytes = ropelib_ws(p) if ws is None else ws
+    return p
+
+
+def ropelib_ws(p):
+    return rfa.lib().rope_decode_workspace_size(ctypes.byref(p))
+
+
+def test_decode_workspace_size(ropelib):
+    p = valid_decode_params()
+    need = ropelib.rope_decode_workspace_size(ctypes.byref(p))
+    # partial O (head_dim floats) plus m and l per (sequence, q head, split)
+    assert need > 0 and need % (4 * 16 * (128 + 2)) == 0
+    splits = need // (4 * 16 * (128 + 2))
+    assert 1 <= splits <= 256
+    p.num_splits = 5
+    assert ropelib.rope_decode_workspace_size(ctypes.byref(p)) == 4 * 16 * 5 * 130 * 4
+    p.num_splits = 300
+    assert ropelib.rope_decode_workspace_size(ctypes.byref(p)) == 0
+    assert ropelib.rope_decode_workspace_size(None) == 0
+    # the automatic split never gives a split fewer than 128 keys
+    p = valid_decode_params(B=1, hq=8, hkv=8, L=300)
+    assert ropelib.rope_decode_workspace_size(ctypes.byref(p)) == 8 * 3 * 130 * 4
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), "ROPE_ERR_ABI"),
+    (dict(rsv=1), "ROPE_ERR_ABI"),
+    (dict(dtype=0), "ROPE_ERR_DTYPE"),
+    (dict(dtype=3), "ROPE_ERR_UNSUPPORTED"),          # no float32 decode kernel
+    (dict(q=None), "ROPE_ERR_NULL"),
+    (dict(k_cache=None), "ROPE_ERR_NULL"),
+    (dict(cache_seqlens=None), "ROPE_ERR_NULL"),
+    (dict(out=None), "ROPE_ERR_NULL"),
+    (dict(sin=None), "ROPE_ERR_NULL"),
+    (dict(hq=6), "ROPE_ERR_SHAPE"),
+    (dict(batch=0), "ROPE_ERR_SHAPE"),
+    (dict(block_size=0), "ROPE_ERR_SHAPE"),
+    (dict(max_seqlen=0), "ROPE_ERR_SHAPE"),
+    (dict(max_seqlen=64 * 16 + 1), "ROPE_ERR_SHAPE"),  # beyond the block table's reach
+    (dict(num_splits=-1), "ROPE_ERR_SHAPE"),
+    (dict(num_splits=257), "ROPE_ERR_LIMIT"),
+    (dict(softmax_scale=0.0), "ROPE_ERR_SHAPE"),
+    (dict(head_dim=96), "ROPE_ERR_UNSUPPORTED"),
+    (dict(q_stride=(16 * 128, 130)), "ROPE_ERR_UNSUPPORTED"),
+    (dict(kc_stride=(16 * 4 * 128, -4 * 128, 128)), "ROPE_ERR_SHAPE"),
+    (dict(out=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
+    (dict(block_table=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
+    (dict(workspace=None), "ROPE_ERR_WORKSPACE"),
+    (dict(workspace=0x100000 + 128), "ROPE_ERR_WORKSPACE"),
+    (dict(workspace_bytes=1024), "ROPE_ERR_WORKSPACE"),
+])
+def test_decode_rejects(ropelib, kw, status):
+    p = mutate(valid_decode_params(), **kw)
+    assert ropelib.rope_decode_attn_fwd(ctypes.byref(p), None) == ST[status]
 
 
 def test_binding_refuses_cpu_tensors(ropelib):
