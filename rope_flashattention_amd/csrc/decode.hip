@@ -10,17 +10,24 @@
 //
 // Partial kernel (decode_partial_kernel): one wavefront per (sequence, kv head, group of
 // up to 32 q heads, key split).  Per 32-key tile:
-//   * S^T = K Q'^T with the 32x32x16 MFMA: the A operand is read straight from the cache,
-//     lane l loading 16 bytes of key pi(l % 32) (the permuted row order below), the B
-//     operand is the rotated, scaled Q' of the group's heads (head = MFMA column), held in
-//     registers for the whole pass; unused columns are zero.
+//   * K and V rows arrive by coalesced 16-byte loads (whole 256-byte rows per 16 lanes;
+//     every load of a tile issued back to back, the next tile's loads issued as soon as
+//     this tile is in LDS) and are stored row-major in a wave-private LDS tile whose
+//     16-byte chunks are XOR-swizzled per row, so the reads below are bank-conflict free.
+//     The split's block-table entries are read once into one register per lane and
+//     fetched per row with a lane shuffle.
+//   * S^T = K Q'^T with the 32x32x16 MFMA: the A operand is LDS row pi(m) of the K tile,
+//     the B operand the rotated, scaled Q' of the group's heads (head = MFMA column) held
+//     in registers for the whole pass; unused columns are zero.
 //   * Permuted rows: MFMA row m holds key pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3), which
 //     makes lane half h hold the scores of the contiguous keys 16h .. 16h+15 of its head, so
 //     the probabilities are already the B operand of the next product.
-//   * Online softmax per head in the log2 domain (scale * log2(e) folded into Q').
-//   * O^T += V^T P^T with the same MFMA; V rows go through a wave-private LDS tile and the
-//     transposing LDS read (ds_read_b64_tr_b16) supplies the V^T operand.
-// The wave writes its unnormalised O, running max m and sum l for its key range to the
+//   * Online softmax per head in the log2 domain (scale * log2(e) folded into Q'); the
+//     reference maximum moves, and O and l are rescaled, only when a tile's maximum
+//     exceeds it by more than 2^8 (P <= 2^8 otherwise).
+//   * O^T += V^T P^T with the same MFMA; the transposing LDS read (ds_read_b64_tr_b16)
+//     supplies the V^T operand.
+// The wave writes its unnormalised O, reference m and sum l for its key range to the
 // workspace.  Combine kernel (decode_combine_kernel): one workgroup per (sequence, q head)
 // merges the splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
 #include "common.h"
@@ -46,6 +53,9 @@ struct DecodeArgs {
     int32_t block_size, max_blocks, num_blocks, max_seqlen;
     float scale_log2;
     int32_t rotate;
+    int32_t chunk;      // keys per split (multiple of 32)
+    int32_t bs_shift;   // log2(block_size) when it is a power of two, else -1
+    int32_t table_regs; // 1: a split's block-table entries fit one register per lane
 };
 
 template <typename T> struct DMma;
@@ -85,25 +95,30 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// element offset (without the head term) of logical token `key` of sequence b
-__device__ __forceinline__ int64_t slot_offset(const DecodeArgs& a, int b, int key, const int64_t (&cs)[3]) {
-    const int lb = key / a.block_size;
-    const int off = key - lb * a.block_size;
-    int pb = a.block_table ? a.block_table[(int64_t)b * a.max_blocks + lb] : b * a.max_blocks + lb;
-    pb = min(max(pb, 0), a.num_blocks - 1);
-    return (int64_t)pb * cs[0] + (int64_t)off * cs[1];
+__device__ __forceinline__ int logical_block(const DecodeArgs& a, int key) {
+    return a.bs_shift >= 0 ? key >> a.bs_shift : key / a.block_size;
+}
+
+// physical block of logical block lb of sequence b, clamped into the cache
+__device__ __forceinline__ int physical_block(const DecodeArgs& a, int b, int lb) {
+    const int pb = a.block_table ? a.block_table[(int64_t)b * a.max_blocks + lb] : b * a.max_blocks + lb;
+    return min(max(pb, 0), a.num_blocks - 1);
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
-    constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
-    constexpr int VP = D + 32;   // padded LDS row of the V tile (elements)
+__global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
+    constexpr int NS = D / 16;        // MFMA k-steps over the head dimension
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;     // rows per coalesced load instruction
+    constexpr int NLD = 32 / RPI;     // load instructions per 32-row tile (= D / 16)
     constexpr float kNegInf = -__builtin_inff();
-    __shared__ __attribute__((aligned(16))) T sV[32 * VP];
+    // K and V tiles, row-major, 16-byte chunks XOR-swizzled per row (conflict-free reads)
+    __shared__ __attribute__((aligned(16))) T sK[32 * D];
+    __shared__ __attribute__((aligned(16))) T sV[32 * D];
 
     const int l = threadIdx.x;
-    const int n = l & 31;          // MFMA column: head of the group
-    const int hh = l >> 5;         // lane half
+    const int n = l & 31;
+    const int hh = l >> 5;
     const int split = blockIdx.x;
     const int kvh = blockIdx.y / a.ngroups;
     const int grp = blockIdx.y - kvh * a.ngroups;
@@ -118,8 +133,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
     chunk = (chunk + 31) & ~31;
     const int k_begin = min(split * chunk, L);
     const int k_end = min(L, k_begin + chunk);
+    const int lb0 = k_begin < k_end ? logical_block(a, k_begin) : 0;
+    int tabv = 0;
+    if (a.table_regs && k_begin < k_end) {
+        const int nlb = logical_block(a, k_end - 1) - lb0 + 1;
+        if (l < nlb) tabv = physical_block(a, b, lb0 + l);
+    }
 
-    // ---- Q'^T operand: rotate-half RoPE in float32, scaled by softmax_scale*log2(e), rounded once
+    // ---- Q'^T operand
     u32x4 qb[NS];
     {
         const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.qs[0] + (int64_t)h * a.qs[1];
@@ -151,9 +172,39 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
 
     const T* kbase = reinterpret_cast<const T*>(a.kc) + (int64_t)kvh * a.kcs[2];
     const T* vbase = reinterpret_cast<const T*>(a.vc) + (int64_t)kvh * a.vcs[2];
-    const int prow = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);   // key of MFMA row n
+    const int prow = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);   // key (LDS row) of MFMA row n
+    const int kswz = (prow & 3) | (((prow >> 4) & 1) << 2);          // its chunk swizzle
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
+    const int ld_row = l / CPR;       // + RPI * i
+    const int ld_chunk = l % CPR;
+
+    // coalesced loads of one 32-key tile: instruction i, lane l -> row RPI*i + l/CPR, chunk l%CPR
+    u32x4 kst[NLD], vst[NLD];
+    auto load_tile = [&](int k0) {
+        // physical block and offset of every row first (no load in flight is waited on
+        // here), then all K and V loads back to back
+        int pb[NLD], off[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int key = min(k0 + RPI * i + ld_row, k_end - 1);
+            const int lb = logical_block(a, key);
+            off[i] = key - lb * a.block_size;
+            pb[i] = lb;
+        }
+        if (a.table_regs) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) pb[i] = __shfl(tabv, pb[i] - lb0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) pb[i] = physical_block(a, b, pb[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            kst[i] = load_chunk<T>(kbase + (int64_t)pb[i] * a.kcs[0] + (int64_t)off[i] * a.kcs[1] + ld_chunk * 8).w;
+            vst[i] = load_chunk<T>(vbase + (int64_t)pb[i] * a.vcs[0] + (int64_t)off[i] * a.vcs[1] + ld_chunk * 8).w;
+        }
+    };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -163,22 +214,29 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
     float m_run = kNegInf;
     float l_half = 0.0f;
 
+    if (k_begin < k_end) load_tile(k_begin);
     for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-        // ---- loads: K row pi(n) as the A operand, V row n into registers (ragged tail clamped)
-        const T* krow = kbase + slot_offset(a, b, min(k0 + prow, k_end - 1), a.kcs);
-        const T* vrow = vbase + slot_offset(a, b, min(k0 + n, k_end - 1), a.vcs);
-        u32x4 ka[NS], va[NS];
+        // ---- staged tile -> LDS (K chunk c of row r at slot c ^ fK(r), V at c ^ fV(r))
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ka[s] = load_chunk<T>(krow + 16 * s + 8 * hh).w;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) va[s] = load_chunk<T>(vrow + 16 * s + 8 * hh).w;
+        for (int i = 0; i < NLD; ++i) {
+            const int r = RPI * i + ld_row;
+            const int fk = (r & 3) | (((r >> 4) & 1) << 2);
+            const int fv = 2 * (r & 3);
+            *reinterpret_cast<u32x4*>(&sK[r * D + 8 * (ld_chunk ^ fk)]) = kst[i];
+            *reinterpret_cast<u32x4*>(&sV[r * D + 8 * (ld_chunk ^ fv)]) = vst[i];
+        }
+        wave_lds_sync();
+        if (k0 + 32 < k_end) load_tile(k0 + 32);   // the next tile streams in while this one is used
 
-        // ---- S^T = K Q'^T
+        // ---- S^T = K Q'^T, A operand from LDS row prow
         f32x16 sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) sacc = DMma<T>::run(ka[s], qb[s], sacc);
+        for (int s = 0; s < NS; ++s) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(&sK[prow * D + 8 * ((2 * s + hh) ^ kswz)]);
+            sacc = DMma<T>::run(ka, qb[s], sacc);
+        }
 
         // ---- online softmax: lane half hh holds keys k0 + 16*hh + i
         const int valid = k_end - (k0 + 16 * hh);
@@ -189,37 +247,40 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
             mt = fmaxf(mt, sacc[i]);
         }
         mt = dec_halves_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_half *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+        }
+        const float m_new = m_run;
         u32x4 pk[2];
         float lt = 0.0f;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float p[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = exp2f(sacc[8 * s + j] - m_new);
+            for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sacc[8 * s + j] - m_new);
             pk[s] = pack<T>(p).w;
             float pr[8];
-            unpack<T>(Chunk8<T>{pk[s]}, pr);   // the rounded values the product uses
+            unpack<T>(Chunk8<T>{pk[s]}, pr);
 #pragma unroll
             for (int j = 0; j < 8; ++j) lt += pr[j];
         }
-        l_half = l_half * alpha + lt;
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+        l_half += lt;
 
-        // ---- V tile through LDS, O^T += V^T P^T
-#pragma unroll
-        for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(&sV[n * VP + 16 * s + 8 * hh]) = va[s];
-        wave_lds_sync();
+        // ---- O^T += V^T P^T, V^T operand by the transposing LDS read
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const T* vp = &sV[(16 * hh + 8 * s + tr_row) * VP + mb * 32 + tr_col];
-                const i16x4 lo = lds_tr16(vp);
-                const i16x4 hi = lds_tr16(vp + 4 * VP);
+                const int r = 16 * hh + 8 * s + tr_row;        // rows r and r + 4, r % 4 == tr_row
+                const int e = mb * 32 + tr_col;                 // element column, 4 elements
+                const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
+                const i16x4 lo = lds_tr16(&sV[r * D + sw]);
+                const i16x4 hi = lds_tr16(&sV[(r + 4) * D + sw]);
                 const u32x4 av = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[mb] = DMma<T>::run(av, pk[s], oacc[mb]);
             }
@@ -252,11 +313,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int h = bh - b * a.hq;
     const int d = threadIdx.x;
     const int64_t p0 = (int64_t)bh * a.nsplit;
+    const int live = a.nsplit;
     float M = -__builtin_inff();
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_m[p0 + s]);
+    for (int s = 0; s < live; ++s) M = fmaxf(M, a.ws_m[p0 + s]);
     float o = 0.0f, lsum = 0.0f;
     if (M != -__builtin_inff()) {
-        for (int s = 0; s < a.nsplit; ++s) {
+        for (int s = 0; s < live; ++s) {
             const float w = exp2f(a.ws_m[p0 + s] - M);   // empty splits: m = -inf, w = 0
             lsum += w * a.ws_l[p0 + s];
             o += w * a.ws_o[(p0 + s) * D + d];
@@ -328,6 +390,12 @@ hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream) {
     a.num_blocks = p->num_blocks;
     a.max_seqlen = p->max_seqlen;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    a.chunk = (((p->max_seqlen + nsplit - 1) / nsplit) + 31) & ~31;
+    a.bs_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == p->block_size) a.bs_shift = sh;
+    // blocks one split can touch: chunk / block_size + 1 (an unaligned start)
+    a.table_regs = (a.chunk / p->block_size + 2) <= 64;
     const int key = (p->dtype == ROPE_DT_BF16 ? 0 : 2) + (p->head_dim == 128 ? 1 : 0);
     switch (key) {
         case 0: launch_typed<__bf16, 64>(a, stream); break;
