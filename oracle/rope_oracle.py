@@ -20,8 +20,11 @@ state.  Page key used in the citations:
   position), 六 (rotation geometry), 八 (RMSNorm), 十一/十二 (MQA/GQA).
 
 Readings taken where the pages are silent (also listed in the design notes):
-rotate-half pairing (dims i and i+D/2 share frequency i, from emb = cat(freq,
-freq)); rotation sign R = [[cos, -sin], [sin, cos]] on (x_i, x_{i+D/2});
+rotate-half pairing by default (dims i and i+D/2 share frequency i, from emb =
+cat(freq, freq)); the interleaved pairing of [RoPE/GQA tutorial, section 六]
+((x_1, x_2), (x_3, x_4), ...: dims 2i and 2i+1 share frequency i, tables hold each
+pair's angle in both of its columns) as the ``pairing="interleaved"`` variant;
+rotation sign R = [[cos, -sin], [sin, cos]] on each pair;
 angles formed in float32 (int32 positions, float32 inverse frequencies);
 contiguous GQA grouping (kv head = q head // group); softmax scale passed in.
 
@@ -55,7 +58,11 @@ __all__ = [
     "kv_rms_norm_rope_cache",
     "cache_slots",
     "decode_attention",
+    "pair_partner",
+    "PAIRINGS",
 ]
+
+PAIRINGS = ("half", "interleaved")
 
 # (precision p incl. the implicit bit, minimum normal exponent emin)
 DTYPE_FORMATS = {"f16": (11, -14), "bf16": (8, -126), "f32": (24, -126)}
@@ -153,76 +160,96 @@ def angles(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32"
     return out
 
 
-def rope_tables(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32"):
+def pair_partner(D: int, pairing: str = "half"):
+    """(partner, sign, freq_index) of every dimension j < D for the given pairing.
+
+    Rotating pair (a, b) by theta gives a' = a cos - b sin, b' = b cos + a sin, so
+    x'_j = x_j cos_j + sign_j * x_partner(j) * sin_j with sign -1 on the first member of
+    the pair.  "half": pair i = (i, i + D/2) (emb = cat(freq, freq)); "interleaved":
+    pair i = (2i, 2i + 1) ([RoPE/GQA tutorial, section 六], adjacent 2-D blocks).
+    freq_index[j] is the frequency (table angle) that dimension j uses.
+    """
+    j = np.arange(D)
+    if pairing == "half":
+        h = D // 2
+        return np.where(j < h, j + h, j - h), np.where(j < h, -1.0, 1.0), j % h
+    if pairing == "interleaved":
+        return j ^ 1, np.where(j % 2 == 0, -1.0, 1.0), j // 2
+    raise ValueError(pairing)
+
+
+def rope_tables(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32", pairing: str = "half"):
     """(sin, cos), each float64 [ntokens, D].
 
     [DynamicNTKOperation, 算子功能分析]: emb = cat((freq, freq), -1); sinOut = emb.sin();
-    cosOut = emb.cos().  Output shape [ntokens, headSize] ([输出]).
+    cosOut = emb.cos().  Output shape [ntokens, headSize] ([输出]).  With
+    pairing="interleaved" column j holds the angle of frequency j // 2 instead.
     """
     freq = angles(pos, inv_freq_b, seq_lens, pos_scale, mode)
-    emb = np.concatenate([freq, freq], axis=-1)
+    D = 2 * freq.shape[1]
+    emb = freq[:, pair_partner(D, pairing)[2]]
     return np.sin(emb), np.cos(emb)
 
 
 # --------------------------------------------------------------------------- rotation
-def rotation_matrix(theta_row) -> np.ndarray:
+def rotation_matrix(theta_row, pairing: str = "half") -> np.ndarray:
     """Explicit D x D rotation for one token, from its D/2 angles.
 
     [RoPE/GQA tutorial, section 六]: the vector is split into 2-D pairs and each pair is
     rotated by a position-dependent angle; [RoPE-fusion blog, section 一]: each token is
-    multiplied by a position-dependent rotation matrix.  Pairs follow the rotate-half
-    layout of emb = cat(freq, freq): pair i is (x_i, x_{i+D/2}) with angle theta_i.
+    multiplied by a position-dependent rotation matrix.  "half": pair i is
+    (x_i, x_{i+D/2}) (the layout of emb = cat(freq, freq)); "interleaved": pair i is
+    (x_{2i}, x_{2i+1}).  Angle theta_i either way.
     """
     theta_row = np.asarray(theta_row, dtype=np.float64)
     half = theta_row.shape[0]
     D = 2 * half
     R = np.zeros((D, D), dtype=np.float64)
     for i in range(half):
+        a, b = (i, i + half) if pairing == "half" else (2 * i, 2 * i + 1)
+        if pairing not in PAIRINGS:
+            raise ValueError(pairing)
         c, s = np.cos(theta_row[i]), np.sin(theta_row[i])
-        R[i, i] = c
-        R[i, i + half] = -s
-        R[i + half, i] = s
-        R[i + half, i + half] = c
+        R[a, a] = c
+        R[a, b] = -s
+        R[b, a] = s
+        R[b, b] = c
     return R
 
 
-def rope_op_matrix(cos_row, sin_row) -> np.ndarray:
+def rope_op_matrix(cos_row, sin_row, pairing: str = "half") -> np.ndarray:
     """Explicit D x D matrix of the Rope op for one token, from its table rows.
 
     [DynamicNTKOperation, 算子上下文]: q, k, sin, cos enter the Rope op, which outputs the
     rotated q, k.  Written out per element: x'_j = x_j cos_j + rh(x)_j sin_j with
-    rh(x) = cat(-x[D/2:], x[:D/2]).  For tables in the cat(freq, freq) form this is the
-    rotation of ``rotation_matrix``; for arbitrary table values it is the same linear map.
+    rh(x) = cat(-x[D/2:], x[:D/2]) for "half" and rh(x)_{2i} = -x_{2i+1},
+    rh(x)_{2i+1} = x_{2i} for "interleaved".  For tables in the matching form this is
+    the rotation of ``rotation_matrix``; for arbitrary table values it is the same map.
     """
     cos_row = np.asarray(cos_row, dtype=np.float64)
     sin_row = np.asarray(sin_row, dtype=np.float64)
     D = cos_row.shape[0]
-    half = D // 2
+    partner, sign, _ = pair_partner(D, pairing)
     M = np.zeros((D, D), dtype=np.float64)
     for j in range(D):
         M[j, j] = cos_row[j]
-        if j < half:
-            M[j, j + half] = -sin_row[j]
-        else:
-            M[j, j - half] = sin_row[j]
+        M[j, partner[j]] = sign[j] * sin_row[j]
     return M
 
 
-def rotate_tokens(x, cos, sin, chunk: int = 512) -> np.ndarray:
+def rotate_tokens(x, cos, sin, chunk: int = 512, pairing: str = "half") -> np.ndarray:
     """Apply each token's explicit Rope-op matrix to x [T, H, D] (float64 out).
 
-    Token t uses rope_op_matrix(cos[t], sin[t]); every head of the token shares it.
-    Matrices are built in token chunks to bound memory.
+    Token t uses rope_op_matrix(cos[t], sin[t], pairing); every head of the token shares
+    it.  Matrices are built in token chunks to bound memory.
     """
     x = np.asarray(x, dtype=np.float64)
     cos = np.asarray(cos, dtype=np.float64)
     sin = np.asarray(sin, dtype=np.float64)
     T, H, D = x.shape
-    half = D // 2
     out = np.empty_like(x)
     idx = np.arange(D)
-    partner = np.where(idx < half, idx + half, idx - half)
-    sign = np.where(idx < half, -1.0, 1.0)
+    partner, sign, _ = pair_partner(D, pairing)
     for t0 in range(0, T, chunk):
         t1 = min(T, t0 + chunk)
         n = t1 - t0
@@ -268,7 +295,7 @@ def _check_packed(q, k, v, seq_lens):
     return T, Hq, Hkv, D
 
 
-def rope_attention(q, k, v, cos, sin, seq_lens, scale: float, causal: bool = True):
+def rope_attention(q, k, v, cos, sin, seq_lens, scale: float, causal: bool = True, pairing: str = "half"):
     """Full oracle: rotate Q and K with their tokens' tables, then attention per
     (sequence, q head).  Packed layout: q [T, Hq, D], k/v [T, Hkv, D], tables [T, D].
 
@@ -278,8 +305,8 @@ def rope_attention(q, k, v, cos, sin, seq_lens, scale: float, causal: bool = Tru
     """
     T, Hq, Hkv, D = _check_packed(q, k, v, seq_lens)
     g = Hq // Hkv
-    qr = rotate_tokens(q, cos, sin)
-    kr = rotate_tokens(k, cos, sin)
+    qr = rotate_tokens(q, cos, sin, pairing=pairing)
+    kr = rotate_tokens(k, cos, sin, pairing=pairing)
     v = np.asarray(v, dtype=np.float64)
     O = np.empty((T, Hq, D), dtype=np.float64)
     lse = np.empty((Hq, T), dtype=np.float64)
@@ -292,7 +319,7 @@ def rope_attention(q, k, v, cos, sin, seq_lens, scale: float, causal: bool = Tru
     return O, lse
 
 
-def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool, samples):
+def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool, samples, pairing: str = "half"):
     """Oracle output rows O[t, h, :] (and lse) for a list of (t, h) samples only.
 
     The same definition as ``rope_attention`` evaluated one query row at a time, so
@@ -312,10 +339,11 @@ def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool,
         kvh = h // g
         key = (b, kvh)
         if key not in cache:
-            kr = rotate_tokens(np.asarray(k[s0:s0 + L, kvh:kvh + 1]), cos[s0:s0 + L], sin[s0:s0 + L])[:, 0]
+            kr = rotate_tokens(np.asarray(k[s0:s0 + L, kvh:kvh + 1]), cos[s0:s0 + L], sin[s0:s0 + L],
+                               pairing=pairing)[:, 0]
             cache[key] = (kr, np.asarray(v[s0:s0 + L, kvh], dtype=np.float64))
         kr, vv = cache[key]
-        qr = rotate_tokens(np.asarray(q[t:t + 1, h:h + 1]), cos[t:t + 1], sin[t:t + 1])[0, 0]
+        qr = rotate_tokens(np.asarray(q[t:t + 1, h:h + 1]), cos[t:t + 1], sin[t:t + 1], pairing=pairing)[0, 0]
         i = t - s0
         n_keys = i + 1 if causal else L
         s = (kr[:n_keys] @ qr) * float(scale)
@@ -338,7 +366,7 @@ def rms_norm(x, gamma, eps: float) -> np.ndarray:
     return np.asarray(gamma, dtype=np.float64) * x / np.sqrt(ms + float(eps))
 
 
-def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
+def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache, pairing: str = "half"):
     """The fused "RMSNorm, RoPE, write to the KV cache" step for new tokens.
 
     The [RoPE-fusion blog] (section 五) names this step (kv_rms_norm_rope_cache) without
@@ -354,7 +382,7 @@ def kv_rms_norm_rope_cache(k, v, gamma, eps, cos, sin, slots, k_cache, v_cache):
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
     kn = k if gamma is None else rms_norm(k, gamma, eps)
-    kr = rotate_tokens(kn, cos, sin)
+    kr = rotate_tokens(kn, cos, sin, pairing=pairing)
     for t, slot in enumerate(np.asarray(slots).tolist()):
         if slot < 0 or slot >= kc.shape[0]:
             continue
@@ -375,7 +403,8 @@ def cache_slots(block_table_row, length: int, block_size: int) -> np.ndarray:
     return table[j // block_size] * block_size + j % block_size
 
 
-def decode_attention(q, cos, sin, k_cache, v_cache, block_table, cache_lens, block_size: int, scale: float):
+def decode_attention(q, cos, sin, k_cache, v_cache, block_table, cache_lens, block_size: int, scale: float,
+                     pairing: str = "half"):
     """One decode step: each sequence's new query attends to every token in its cache.
 
     The query q[b, h] (one new token per sequence) is rotated with its table row
@@ -393,7 +422,7 @@ def decode_attention(q, cos, sin, k_cache, v_cache, block_table, cache_lens, blo
     B, Hq, D = q.shape
     Hkv = kc.shape[1]
     g = Hq // Hkv
-    qr = rotate_tokens(q, cos, sin)
+    qr = rotate_tokens(q, cos, sin, pairing=pairing)
     out = np.zeros((B, Hq, D))
     lse = np.zeros((B, Hq))
     for b in range(B):

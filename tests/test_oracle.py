@@ -101,6 +101,23 @@ def test_angles_fp32_rounding():
     check_angles_fp32(orc.angles)
 
 
+def test_angles_exact_mode_error_bound():
+    # exact mode: (p / s) * f in float64, within 2 float64 rounding errors of the real product
+    mpmath.mp.dps = 40
+    r = rng(13)
+    pos = np.array([0, 1, 4095, 65535, 1 << 20, (1 << 24) - 3, 250000], dtype=np.int32)
+    f = r.uniform(1e-6, 1.0, size=(1, 6)).astype(np.float32)
+    for scale in (1.0, 2.0, 3.0):
+        got = orc.angles(pos, f, [pos.size], scale, "exact")
+        for t in range(pos.size):
+            for i in range(f.shape[1]):
+                exact = mpmath.mpf(int(pos[t])) / mpmath.mpf(scale) * mpmath.mpf(float(f[0, i]))
+                assert abs(mpmath.mpf(float(got[t, i])) - exact) <= 2 * 2.0 ** -53 * abs(exact) + 1e-300
+        # and the float32 mode differs from it by at most the two float32 roundings
+        g32 = orc.angles(pos, f, [pos.size], scale, "fp32")
+        assert np.all(np.abs(g32 - got) <= 2 * 2.0 ** -24 * np.abs(got) + 1e-30)
+
+
 def check_table_structure(rope_tables):
     r = rng(2)
     seq_lens = [7, 4]
@@ -182,6 +199,87 @@ def check_relative_position(rope_tables, rotate_tokens):
 
 def test_relative_position():
     check_relative_position(orc.rope_tables, orc.rotate_tokens)
+
+
+# --------------------------------------------------------------------------- interleaved pairing
+def _even_odd_perm(D):
+    """Indices that gather the rotate-half layout from the interleaved one: x_half = x_int[perm]."""
+    return np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+
+
+def check_interleaved(rotation_matrix, rope_op_matrix, rotate_tokens, rope_tables):
+    r = rng(11)
+    D = 16
+    theta = r.uniform(-20, 20, size=D // 2)
+    Ri = rotation_matrix(theta, "interleaved")
+    # by hand: pair 0 is (x_0, x_1), pair 3 is (x_6, x_7)
+    for i in (0, 3):
+        e = np.zeros(D)
+        e[2 * i] = 1.0
+        want = np.zeros(D)
+        want[2 * i], want[2 * i + 1] = math.cos(theta[i]), math.sin(theta[i])
+        assert np.max(np.abs(Ri @ e - want)) < 1e-15
+        e = np.zeros(D)
+        e[2 * i + 1] = 1.0
+        want = np.zeros(D)
+        want[2 * i], want[2 * i + 1] = -math.sin(theta[i]), math.cos(theta[i])
+        assert np.max(np.abs(Ri @ e - want)) < 1e-15
+    # the same rotation as rotate-half, seen through the even/odd permutation
+    perm = _even_odd_perm(D)
+    P = np.eye(D)[perm]                                   # x_half = P x_int
+    assert np.max(np.abs(Ri - P.T @ rotation_matrix(theta, "half") @ P)) < 1e-15
+    # tables: both columns of a pair hold its angle; a column permutation of the half tables
+    seq = [9]
+    pos = np.arange(9, dtype=np.int32) * 37
+    f = orc.inv_freq(1e4, D)[None, :]
+    si, ci = rope_tables(pos, f, seq, 1.0, "fp32", "interleaved")
+    sh, ch = rope_tables(pos, f, seq, 1.0, "fp32", "half")
+    assert np.array_equal(si[:, 0::2], si[:, 1::2]) and np.array_equal(ci[:, 0::2], ci[:, 1::2])
+    assert np.array_equal(si[:, 0::2], sh[:, :D // 2]) and np.array_equal(ci[:, 0::2], ch[:, :D // 2])
+    # the Rope op on interleaved tables is the interleaved rotation
+    emb = np.repeat(theta, 2)
+    assert np.max(np.abs(rope_op_matrix(np.cos(emb), np.sin(emb), "interleaved") - Ri)) < 1e-15
+    # second formulation: x*cos + rotate_every_two(x)*sin, rotate_every_two(x) = (-x1, x0, -x3, x2, ...)
+    x = r.standard_normal((4, 3, D))
+    cos = r.uniform(-1, 1, size=(4, D))
+    sin = r.uniform(-1, 1, size=(4, D))
+    rt = np.empty_like(x)
+    rt[..., 0::2] = -x[..., 1::2]
+    rt[..., 1::2] = x[..., 0::2]
+    want = x * cos[:, None, :] + rt * sin[:, None, :]
+    assert np.max(np.abs(rotate_tokens(x, cos, sin, pairing="interleaved") - want)) < 1e-14
+
+
+def test_interleaved_pairing():
+    check_interleaved(orc.rotation_matrix, orc.rope_op_matrix, orc.rotate_tokens, orc.rope_tables)
+
+
+def test_interleaved_relative_position_and_attention():
+    r = rng(12)
+    D = 32
+    f = orc.inv_freq(1e4, D)[None, :]
+    pos = np.arange(0, 700, dtype=np.int32)
+    s, c = orc.rope_tables(pos, f, [pos.size], 1.0, "exact", "interleaved")
+    q = r.standard_normal((1, 1, D))
+    k = r.standard_normal((1, 1, D))
+
+    def score(m, n):
+        return (orc.rotate_tokens(q, c[m:m + 1], s[m:m + 1], pairing="interleaved")[0, 0]
+                @ orc.rotate_tokens(k, c[n:n + 1], s[n:n + 1], pairing="interleaved")[0, 0])
+
+    for m, n, shift in [(5, 2, 100), (300, 17, 380), (9, 40, 600)]:
+        assert abs(score(m, n) - score(m + shift, n + shift)) <= 1e-12 * max(1.0, abs(score(m, n)))
+    # attention with interleaved pairs = rotate-half attention on even/odd-permuted q and k
+    L, Hq, Hkv = 23, 4, 2
+    qs = r.standard_normal((L, Hq, D))
+    ks = r.standard_normal((L, Hkv, D))
+    vs = r.standard_normal((L, Hkv, D))
+    si, ci = orc.rope_tables(np.arange(L, dtype=np.int32), f, [L], 1.0, "fp32", "interleaved")
+    sh, ch = orc.rope_tables(np.arange(L, dtype=np.int32), f, [L], 1.0, "fp32", "half")
+    perm = _even_odd_perm(D)
+    oi, li = orc.rope_attention(qs, ks, vs, ci, si, [L], 0.3, True, "interleaved")
+    oh, lh = orc.rope_attention(qs[..., perm], ks[..., perm], vs, ch, sh, [L], 0.3, True, "half")
+    assert np.max(np.abs(oi - oh)) < 1e-12 and np.max(np.abs(li - lh)) < 1e-12
 
 
 # --------------------------------------------------------------------------- attention
@@ -602,6 +700,27 @@ def _mut_decode_drops_last(q, cos, sin, k_cache, v_cache, block_table, cache_len
     return orc.decode_attention(q, cos, sin, k_cache, v_cache, block_table, lens, block_size, scale)
 
 
+def _mut_rotation_interleaved_sign(theta_row, pairing="half"):
+    return orc.rotation_matrix(-np.asarray(theta_row), pairing) if pairing == "interleaved" \
+        else orc.rotation_matrix(theta_row, pairing)
+
+
+def _mut_tables_interleaved_as_half(pos, inv_freq_b, seq_lens, pos_scale=1.0, mode="fp32", pairing="half"):
+    return orc.rope_tables(pos, inv_freq_b, seq_lens, pos_scale, mode, "half")
+
+
+def _mut_rotate_tokens_interleaved_swapped(x, cos, sin, chunk=512, pairing="half"):
+    # partner taken two dims away instead of the adjacent one
+    if pairing != "interleaved":
+        return orc.rotate_tokens(x, cos, sin, chunk, pairing)
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    j = np.arange(D)
+    partner = (j + 2) % D
+    sign = np.where(j % 2 == 0, -1.0, 1.0)
+    return x * np.asarray(cos)[:, None, :] + sign * x[..., partner] * np.asarray(sin)[:, None, :]
+
+
 def _mut_rope_attention_gqa_strided(q, k, v, cos, sin, seq_lens, scale, causal=True):
     hq, hkv = q.shape[1], k.shape[1]
     idx = np.arange(hq) % hkv                      # strided instead of contiguous groups
@@ -634,6 +753,14 @@ def _mut_rope_attention_no_segments(q, k, v, cos, sin, seq_lens, scale, causal=T
     ("decode block and offset swapped", lambda g: check_decode(orc.decode_attention, _mut_cache_slots_swapped)),
     ("decode GQA by modulo", lambda g: check_decode(_mut_decode_gqa_modulo, orc.cache_slots)),
     ("decode drops the newest key", lambda g: check_decode(_mut_decode_drops_last, orc.cache_slots)),
+    ("interleaved rotation sign", lambda g: check_interleaved(_mut_rotation_interleaved_sign, orc.rope_op_matrix,
+                                                              orc.rotate_tokens, orc.rope_tables)),
+    ("interleaved tables in half layout", lambda g: check_interleaved(orc.rotation_matrix, orc.rope_op_matrix,
+                                                                      orc.rotate_tokens,
+                                                                      _mut_tables_interleaved_as_half)),
+    ("interleaved partner two away", lambda g: check_interleaved(orc.rotation_matrix, orc.rope_op_matrix,
+                                                                 _mut_rotate_tokens_interleaved_swapped,
+                                                                 orc.rope_tables)),
 ])
 def test_pins_reject_planted_mistakes(name, run, golden_dir):
     with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
