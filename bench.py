@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 METRIC = "fused RoPE+FlashAttn fwd TFLOP/s and % bf16 MFMA peak; rope_tables GB/s"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA peaks (f32: matrix fp32)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.hip", "rope_flashattention_amd/csrc/common.h"]
+KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.h", "rope_flashattention_amd/csrc/common.h"]
 
 
 def source_hash(paths):
@@ -253,6 +253,27 @@ def main():
         comp["unfused_ms"] = round(ms + ms_plain, 4)
         comp["fused_ms"] = round(att_ms, 4)
         del oq, ok
+        # RoPE variants of the fused kernel on the same workload: interleaved pairs (tables
+        # from rope_tables_ex), and table values formed inside the kernel (no table read, no
+        # table pass) for both pairings
+        if not w.varlen:
+            vpos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)
+            vf = torch.from_numpy(rfa.inv_freq(w.base, w.head_dim, [w.seqlen], w.trained_len)).to(dev)
+            isin, icos = rfa.rope_tables(vpos, vf, [w.seqlen], w.head_dim, w.pos_scale, w.torch_dtype,
+                                         pairing="interleaved")
+            vkw = dict(causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+            for name, fn in (
+                    ("interleaved_tables", lambda: rfa.rope_flash_attn_fwd(q, k, v, icos, isin, pairing="interleaved",
+                                                                           **vkw)),
+                    ("formed_tables_half", lambda: rfa.rope_flash_attn_fwd(q, k, v, None, None, pos=vpos, inv_freq=vf,
+                                                                           pos_scale=w.pos_scale, **vkw)),
+                    ("formed_tables_interleaved", lambda: rfa.rope_flash_attn_fwd(
+                        q, k, v, None, None, pos=vpos, inv_freq=vf, pos_scale=w.pos_scale, pairing="interleaved",
+                        **vkw))):
+                fn()
+                vms = time_events(fn, 10, torch)
+                comp[f"fused_{name}_ms"] = round(vms, 4)
+                comp[f"fused_{name}_tflops"] = round(flops / (vms * 1e-3) / 1e12, 2)
         # rope_tables at the op's limits: batch 16, ntokens 256000 (sequences of 16000 tokens),
         # head_size 2048 (2.1 GB written) and 512; buffers warmed up before timing
         lens = np.full(16, 16000, dtype=np.int32)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ROPE_FA_ABI_VERSION 1
+#define ROPE_FA_ABI_VERSION 2
 
 typedef enum rope_status {
     ROPE_OK = 0,
@@ -58,6 +58,29 @@ typedef enum rope_dtype {
     ROPE_DT_BF16 = 2,
     ROPE_DT_F32 = 3
 } rope_dtype;
+
+/* Which coordinates form the 2-D pairs that RoPE rotates (pair i turns by angle
+ * theta_i = position * inv_freq[i]).
+ *   HALF:        pair i = (x[i], x[i + D/2]); tables hold theta_i in columns i and i + D/2
+ *                (emb = cat(freq, freq), [DynamicNTKOperation], 算子功能分析).
+ *   INTERLEAVED: pair i = (x[2i], x[2i + 1]) (the adjacent 2-D blocks of the [RoPE/GQA
+ *                tutorial], section 六); tables hold theta_i in columns 2i and 2i + 1.
+ * Either way the rotation of a pair (a, b) is a' = a*cos - b*sin, b' = b*cos + a*sin,
+ * each output using the table values of its own column. */
+typedef enum rope_pairing {
+    ROPE_PAIR_HALF = 0,
+    ROPE_PAIR_INTERLEAVED = 1
+} rope_pairing;
+
+/* How table angles are formed.
+ *   F32:   fl32(fl32(pos / pos_scale) * inv_freq) and float32 sin/cos (the table op's own
+ *          input types, int32 positions and float32 inverse frequencies).
+ *   EXACT: (pos / pos_scale) * inv_freq and sin/cos in float64, rounded once to the output
+ *          type: no float32 angle rounding, whose error grows with the position. */
+typedef enum rope_angle_mode {
+    ROPE_ANGLE_F32 = 0,
+    ROPE_ANGLE_EXACT = 1
+} rope_angle_mode;
 
 /* Limits of the table op ([DynamicNTKOperation], 约束说明). */
 #define ROPE_MAX_HEAD_SIZE 2048   /* head_size <= 2048 and a multiple of 32 */
@@ -113,6 +136,17 @@ rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t
                         rope_dtype out_dtype, void* sin_out, void* cos_out, void* hip_stream);
 
 /*
+ * rope_tables_ex — rope_tables with a pairing (table column layout) and an angle mode.
+ * rope_tables(...) is rope_tables_ex(..., ROPE_PAIR_HALF, ROPE_ANGLE_F32, ...).  All other
+ * arguments, limits and errors as for rope_tables; pairing or angle_mode out of range ->
+ * ROPE_ERR_UNSUPPORTED.  One kernel launch.
+ */
+rope_status rope_tables_ex(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens,
+                           int32_t batch, int32_t ntokens, int32_t head_size, float pos_scale,
+                           rope_dtype out_dtype, rope_pairing pairing, rope_angle_mode angle_mode,
+                           void* sin_out, void* cos_out, void* hip_stream);
+
+/*
  * Parameters of rope_qk and rope_flash_attn_fwd.
  *
  * Q has hq heads, K and V have hkv heads; hq % hkv == 0 and q head h reads kv head
@@ -132,6 +166,15 @@ rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t
  *   dense:  s when table_seq_rows == 0 (one table shared by every sequence), else
  *           b * table_seq_rows + s (table_seq_rows >= seqlen).
  * cos == sin == NULL disables the rotation (plain attention; rope_flash_attn_fwd only).
+ *
+ * Tables formed in the kernel: with cos == sin == NULL and pos != NULL the kernels compute
+ * each table value they use from pos (int32, one per table row, rows indexed exactly as
+ * the table rows above) and inv_freq ([inv_freq_rows, head_dim/2] float; row b serves
+ * sequence b, or row 0 serves all when inv_freq_rows == 1), in ROPE_ANGLE_F32 mode, and
+ * round it to dtype: the results equal those of the same call with the tables that
+ * rope_tables_ex(pos, inv_freq, ..., pos_scale, dtype, pairing, ROPE_ANGLE_F32) writes
+ * (the table computation of the [RoPE-fusion blog], section 5.1, done inside the fused
+ * operator).  table_dtype and table_seq_rows keep their meaning for the row indexing.
  */
 typedef struct rope_attn_params {
     uint32_t struct_size;       /* = sizeof(rope_attn_params), else ROPE_ERR_ABI */
@@ -163,6 +206,12 @@ typedef struct rope_attn_params {
     int32_t table_seq_rows;     /* dense only, see above */
     float softmax_scale;        /* multiplies q.k before the softmax; the caller passes 1/sqrt(head_dim)
                                    ([FlashAttention blog]: Softmax(QK^T/sqrt(d))V) */
+    rope_pairing pairing;       /* pair layout of the rotation and of the tables */
+    const int32_t* pos;         /* DEVICE int32 [table rows] or NULL: positions for tables formed in
+                                   the kernel (used only when cos == sin == NULL) */
+    const float* inv_freq;      /* DEVICE float [inv_freq_rows, head_dim/2] (with pos) */
+    int32_t inv_freq_rows;      /* 1 or batch (with pos) */
+    float pos_scale;            /* linear position scaling, finite and > 0 (with pos) */
     uint8_t rsv[16];            /* reserved, must be zero (cf. the rsv[] of DynamicNTKParam) */
 } rope_attn_params;
 
@@ -173,8 +222,9 @@ typedef struct rope_attn_params {
  * section 二.  For every token and head of q and of k, with x a head row of length
  * D = head_dim and the token's table rows cos, sin:
  *   x'[j] = x[j]*cos[j] + rotate_half(x)[j]*sin[j],  rotate_half(x) = cat(-x[D/2:], x[:D/2])
+ * (ROPE_PAIR_HALF; with ROPE_PAIR_INTERLEAVED the partner of x[2i] is x[2i+1] instead),
  * computed in float32 and rounded to nearest-even into dtype.  All D table columns are
- * read.  Uses q, k, out_q, out_k, cos, sin, table_dtype, table_seq_rows, batch, hq, hkv,
+ * read (or formed in the kernel from pos and inv_freq, see above).  Uses q, k, out_q, out_k, cos, sin, table_dtype, table_seq_rows, batch, hq, hkv,
  * head_dim, seqlen / cu_seqlens / ntokens, q_stride (also for out_q), k_stride (also for
  * out_k).  In-place (out_q == q, out_k == k) is allowed; other overlap is not.
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
@@ -189,8 +239,10 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
  *   q' = rope(q[b, s, h]),  k'_j = rope(k[b, j, h / g])   (the rope_qk formula)
  *   out[b, s, h] = sum_j softmax_j(softmax_scale * q'.k'_j) v[b, j, h / g]
  * over keys j <= s when causal (within the sequence), else all j < length.
- * The kernel reads only table columns [0, head_dim/2) and applies them to both halves:
- * tables must be in the cat(freq, freq) form that rope_tables produces (unchecked).
+ * With ROPE_PAIR_HALF the kernel reads only table columns [0, head_dim/2) and applies them
+ * to both halves: tables must be in the cat(freq, freq) form that rope_tables produces
+ * (unchecked).  With ROPE_PAIR_INTERLEAVED all columns are read.  Tables may instead be
+ * formed in the kernel from pos and inv_freq (see the parameters).
  * Supported: head_dim 64 or 128 with F16, BF16 (fp16/bf16 matrix cores with float32
  * accumulation); head_dim 64 with F32 (float32 matrix cores).  Optional lse output (see above).
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
@@ -236,7 +288,8 @@ typedef struct rope_kv_cache_params {
     int64_t v_stride[2];
     int64_t kc_stride[3];       /* {block, offset in block, head} in elements */
     int64_t vc_stride[3];
-    uint8_t rsv[16];            /* reserved, must be zero */
+    rope_pairing pairing;       /* pair layout of the rotation and of the tables */
+    uint8_t rsv[12];            /* reserved, must be zero */
 } rope_kv_cache_params;
 
 /*
@@ -298,7 +351,8 @@ typedef struct rope_decode_params {
     int64_t o_stride[2];
     int64_t kc_stride[3];         /* {block, offset in block, head} in elements */
     int64_t vc_stride[3];
-    uint8_t rsv[16];              /* reserved, must be zero */
+    rope_pairing pairing;         /* pair layout of the query rotation and of its tables */
+    uint8_t rsv[12];              /* reserved, must be zero */
 } rope_decode_params;
 
 /*

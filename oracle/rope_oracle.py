@@ -187,7 +187,7 @@ def rope_tables(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "
     """
     freq = angles(pos, inv_freq_b, seq_lens, pos_scale, mode)
     D = 2 * freq.shape[1]
-    emb = freq[:, pair_partner(D, pairing)[2]]
+    emb = np.ascontiguousarray(freq[:, pair_partner(D, pairing)[2]])
     return np.sin(emb), np.cos(emb)
 
 

@@ -33,6 +33,8 @@ __all__ = [
     "RopeDecodeParams",
     "STATUS",
     "DTYPE",
+    "PAIRING",
+    "ANGLE_MODE",
     "LIB_PATH",
 ]
 
@@ -41,7 +43,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_fa.
 STATUS = {0: "ROPE_OK", 1: "ROPE_ERR_NULL", 2: "ROPE_ERR_SHAPE", 3: "ROPE_ERR_DTYPE", 4: "ROPE_ERR_LIMIT",
           5: "ROPE_ERR_UNSUPPORTED", 6: "ROPE_ERR_ABI", 7: "ROPE_ERR_HIP", 8: "ROPE_ERR_WORKSPACE"}
 DTYPE = {None: 0, torch.float16: 1, torch.bfloat16: 2, torch.float32: 3}
-ABI_VERSION = 1
+PAIRING = {"half": 0, "interleaved": 1}
+ANGLE_MODE = {"f32": 0, "exact": 1}
+ABI_VERSION = 2
 
 
 class RopeError(RuntimeError):
@@ -82,6 +86,11 @@ class RopeAttnParams(ctypes.Structure):
         ("table_dtype", ctypes.c_int),
         ("table_seq_rows", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("pairing", ctypes.c_int),
+        ("pos", ctypes.c_void_p),
+        ("inv_freq", ctypes.c_void_p),
+        ("inv_freq_rows", ctypes.c_int32),
+        ("pos_scale", ctypes.c_float),
         ("rsv", ctypes.c_uint8 * 16),
     ]
 
@@ -110,7 +119,8 @@ class RopeKvCacheParams(ctypes.Structure):
         ("v_stride", ctypes.c_int64 * 2),
         ("kc_stride", ctypes.c_int64 * 3),
         ("vc_stride", ctypes.c_int64 * 3),
-        ("rsv", ctypes.c_uint8 * 16),
+        ("pairing", ctypes.c_int),
+        ("rsv", ctypes.c_uint8 * 12),
     ]
 
 
@@ -145,7 +155,8 @@ class RopeDecodeParams(ctypes.Structure):
         ("o_stride", ctypes.c_int64 * 2),
         ("kc_stride", ctypes.c_int64 * 3),
         ("vc_stride", ctypes.c_int64 * 3),
-        ("rsv", ctypes.c_uint8 * 16),
+        ("pairing", ctypes.c_int),
+        ("rsv", ctypes.c_uint8 * 12),
     ]
 
 
@@ -165,6 +176,9 @@ def lib() -> ctypes.CDLL:
     L.rope_inv_freq.restype = st
     L.rope_tables.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, ctypes.c_int, vp, vp, vp]
     L.rope_tables.restype = st
+    L.rope_tables_ex.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 vp, vp, vp]
+    L.rope_tables_ex.restype = st
     L.rope_qk.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
     L.rope_qk.restype = st
     L.rope_flash_attn_fwd.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
@@ -228,8 +242,9 @@ def inv_freq(base: float, head_size: int, seq_lens: Optional[Sequence[int]] = No
 # --------------------------------------------------------------------------- rope_tables
 def rope_tables(pos: torch.Tensor, inv_freq_dev: torch.Tensor, seq_lens: Sequence[int], head_size: int,
                 pos_scale: float = 1.0, out_dtype=torch.bfloat16, sin_out: Optional[torch.Tensor] = None,
-                cos_out: Optional[torch.Tensor] = None):
-    """(sin, cos) tables [ntokens, head_size] on the GPU (rope_tables)."""
+                cos_out: Optional[torch.Tensor] = None, *, pairing: str = "half", angle_mode: str = "f32"):
+    """(sin, cos) tables [ntokens, head_size] on the GPU (rope_tables; rope_tables_ex for a
+    pairing or angle mode other than the defaults)."""
     _need_cuda(pos, inv_freq_dev, sin_out, cos_out)
     if pos.dtype != torch.int32 or inv_freq_dev.dtype != torch.float32:
         raise ValueError("pos must be int32 and inv_freq float32")
@@ -246,10 +261,16 @@ def rope_tables(pos: torch.Tensor, inv_freq_dev: torch.Tensor, seq_lens: Sequenc
     for t in (sin_out, cos_out):
         if t.shape != (n, head_size) or not t.is_contiguous() or t.dtype != out_dtype:
             raise ValueError("sin_out/cos_out must be contiguous [ntokens, head_size] of out_dtype")
-    st = lib().rope_tables(pos.data_ptr(), inv_freq_dev.data_ptr(), sl.ctypes.data, int(sl.size), n, int(head_size),
-                           float(pos_scale), DTYPE.get(out_dtype, -1), sin_out.data_ptr(), cos_out.data_ptr(),
-                           _stream(pos))
-    _check("rope_tables", st)
+    if pairing == "half" and angle_mode == "f32":
+        st = lib().rope_tables(pos.data_ptr(), inv_freq_dev.data_ptr(), sl.ctypes.data, int(sl.size), n,
+                               int(head_size), float(pos_scale), DTYPE.get(out_dtype, -1), sin_out.data_ptr(),
+                               cos_out.data_ptr(), _stream(pos))
+        _check("rope_tables", st)
+    else:
+        st = lib().rope_tables_ex(pos.data_ptr(), inv_freq_dev.data_ptr(), sl.ctypes.data, int(sl.size), n,
+                                  int(head_size), float(pos_scale), DTYPE.get(out_dtype, -1), PAIRING[pairing],
+                                  ANGLE_MODE[angle_mode], sin_out.data_ptr(), cos_out.data_ptr(), _stream(pos))
+        _check("rope_tables_ex", st)
     return sin_out, cos_out
 
 
@@ -274,6 +295,18 @@ def _dims(t: torch.Tensor, layout: str):
     if layout == "TND":
         return 1, t.shape[0], t.shape[1], t.shape[2]
     raise ValueError(f"unknown layout {layout}")
+
+
+def _gen_tables(p, pos, inv_freq, pos_scale, D):
+    """Fill the in-kernel table fields (positions + inverse frequencies)."""
+    if pos.dtype != torch.int32 or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32")
+    if inv_freq is None or inv_freq.dtype != torch.float32 or not inv_freq.is_contiguous() \
+            or inv_freq.shape[-1] != D // 2:
+        raise ValueError("inv_freq must be contiguous float32 [rows, head_dim/2]")
+    p.pos, p.inv_freq = pos.data_ptr(), inv_freq.data_ptr()
+    p.inv_freq_rows = inv_freq.numel() // (D // 2)
+    p.pos_scale = float(pos_scale)
 
 
 def _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows, batch=None):
@@ -320,12 +353,20 @@ def _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows, batc
 
 
 # --------------------------------------------------------------------------- rope_qk
-def rope_qk(q: torch.Tensor, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, *, layout: str = "BNSD",
-            cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None, table_seq_rows: int = 0,
-            out_q: Optional[torch.Tensor] = None, out_k: Optional[torch.Tensor] = None):
-    """Rotated (q', k') written to out_q / out_k (new tensors like q / k by default)."""
-    _need_cuda(q, k, cos, sin, cu_seqlens, out_q, out_k)
+def rope_qk(q: torch.Tensor, k: torch.Tensor, cos: Optional[torch.Tensor], sin: Optional[torch.Tensor], *,
+            layout: str = "BNSD", cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+            table_seq_rows: int = 0, out_q: Optional[torch.Tensor] = None, out_k: Optional[torch.Tensor] = None,
+            pairing: str = "half", pos: Optional[torch.Tensor] = None, inv_freq: Optional[torch.Tensor] = None,
+            pos_scale: float = 1.0):
+    """Rotated (q', k') written to out_q / out_k (new tensors like q / k by default).
+
+    With cos = sin = None and pos / inv_freq given, the kernel forms the table values itself.
+    """
+    _need_cuda(q, k, cos, sin, cu_seqlens, out_q, out_k, pos, inv_freq)
     p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    p.pairing = PAIRING[pairing]
+    if cos is None and pos is not None:
+        _gen_tables(p, pos, inv_freq, pos_scale, p.head_dim)
     out_q = torch.empty_like(q) if out_q is None else out_q
     out_k = torch.empty_like(k) if out_k is None else out_k
     if out_q.shape != q.shape or out_k.shape != k.shape or _strides(out_q, layout) != _strides(q, layout) \
@@ -341,10 +382,19 @@ def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: 
                         sin: Optional[torch.Tensor] = None, *, causal: bool = True,
                         softmax_scale: Optional[float] = None, layout: str = "BNSD",
                         cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
-                        table_seq_rows: int = 0, return_lse: bool = False, out: Optional[torch.Tensor] = None):
-    """Attention output (and lse [hq, ntokens] float32 if asked); cos = sin = None: no rotation."""
-    _need_cuda(q, k, v, cos, sin, cu_seqlens, out)
+                        table_seq_rows: int = 0, return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                        pairing: str = "half", pos: Optional[torch.Tensor] = None,
+                        inv_freq: Optional[torch.Tensor] = None, pos_scale: float = 1.0):
+    """Attention output (and lse [hq, ntokens] float32 if asked).
+
+    cos = sin = None: no rotation, unless pos / inv_freq are given, in which case the kernel
+    forms the table values itself.
+    """
+    _need_cuda(q, k, v, cos, sin, cu_seqlens, out, pos, inv_freq)
     p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    p.pairing = PAIRING[pairing]
+    if cos is None and pos is not None:
+        _gen_tables(p, pos, inv_freq, pos_scale, p.head_dim)
     if v.shape != k.shape or v.dtype != q.dtype:
         raise ValueError("v must match k")
     out = torch.empty_like(q) if out is None else out
@@ -378,7 +428,7 @@ def _cache_strides(c: torch.Tensor, cache_layout: str):
 def rope_kv_rms_norm_rope_cache(k: torch.Tensor, v: Optional[torch.Tensor], cos: torch.Tensor, sin: torch.Tensor,
                                 slots: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], *,
                                 gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
-                                cache_layout: str = "BSND"):
+                                cache_layout: str = "BSND", pairing: str = "half"):
     """RMSNorm (if gamma is given) + RoPE of k [T, hkv, D], written with v into the caches at ``slots``.
 
     Caches are [num_blocks, block_size, hkv, D] ("BSND") or [num_blocks, hkv, block_size, D]
@@ -397,6 +447,7 @@ def rope_kv_rms_norm_rope_cache(k: torch.Tensor, v: Optional[torch.Tensor], cos:
     p = RopeKvCacheParams()
     p.struct_size = ctypes.sizeof(RopeKvCacheParams)
     p.dtype = DTYPE.get(k.dtype, -1)
+    p.pairing = PAIRING[pairing]
     p.k, p.k_cache = k.data_ptr(), k_cache.data_ptr()
     p.k_stride[:] = (k.stride(0), k.stride(1))
     p.kc_stride[:] = kcs
@@ -428,7 +479,7 @@ def rope_kv_rms_norm_rope_cache(k: torch.Tensor, v: Optional[torch.Tensor], cos:
 
 # --------------------------------------------------------------------------- rope_decode_attn_fwd
 def _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, max_seqlen, softmax_scale,
-                   cache_layout, num_splits):
+                   cache_layout, num_splits, pairing="half"):
     if q.dim() != 3 or q.stride(2) != 1:
         raise ValueError("q must be [batch, hq, head_dim] with a unit head_dim stride")
     B, Hq, D = q.shape
@@ -440,6 +491,7 @@ def _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, ma
     p = RopeDecodeParams()
     p.struct_size = ctypes.sizeof(RopeDecodeParams)
     p.dtype = DTYPE.get(q.dtype, -1)
+    p.pairing = PAIRING[pairing]
     p.q, p.k_cache, p.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
     if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_contiguous() or cache_seqlens.numel() != B:
         raise ValueError("cache_seqlens must be contiguous int32 [batch]")
@@ -481,7 +533,7 @@ def rope_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          max_seqlen: int, block_table: Optional[torch.Tensor] = None,
                          softmax_scale: Optional[float] = None, cache_layout: str = "BSND", num_splits: int = 0,
                          return_lse: bool = False, out: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None):
+                         workspace: Optional[torch.Tensor] = None, pairing: str = "half"):
     """Decode-step attention of q [batch, hq, D] (rotated with cos/sin [batch, D]) over the caches.
 
     Caches as in ``rope_kv_rms_norm_rope_cache``; block_table int32 [batch, max_blocks] or None
@@ -490,7 +542,7 @@ def rope_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     """
     _need_cuda(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, out, workspace)
     p = _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, max_seqlen, softmax_scale,
-                       cache_layout, num_splits)
+                       cache_layout, num_splits, pairing)
     need = int(lib().rope_decode_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

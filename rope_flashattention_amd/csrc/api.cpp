@@ -17,7 +17,7 @@
 namespace ropefa {
 hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
                               int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype,
-                              void* sin_out, void* cos_out, hipStream_t stream);
+                              int pairing, int angle_mode, void* sin_out, void* cos_out, hipStream_t stream);
 hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream);
@@ -33,6 +33,8 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_dtype(rope_dtype dt) { return dt == ROPE_DT_F16 || dt == ROPE_DT_BF16 || dt == ROPE_DT_F32; }
+
+bool valid_pairing(rope_pairing pr) { return pr == ROPE_PAIR_HALF || pr == ROPE_PAIR_INTERLEAVED; }
 
 // Strides {batch, token, head, dim}: dim must be 1; the others non-negative and 16-byte multiples.
 rope_status check_strides(const int64_t s[4], int elem_bytes, bool varlen) {
@@ -52,14 +54,25 @@ rope_status check_params(const rope_attn_params* p, bool attention) {
     for (unsigned char c : p->rsv)
         if (c) return ROPE_ERR_ABI;
     if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
+    if (!valid_pairing(p->pairing)) return ROPE_ERR_UNSUPPORTED;
     if (!p->q || !p->k) return ROPE_ERR_NULL;
+    if ((p->cos == nullptr) != (p->sin == nullptr)) return ROPE_ERR_NULL;
+    const bool gen = p->cos == nullptr && p->pos != nullptr;  // tables formed in the kernel
     if (attention) {
         if (!p->v || !p->out) return ROPE_ERR_NULL;
     } else {
         if (!p->out_q || !p->out_k) return ROPE_ERR_NULL;
-        if (!p->cos || !p->sin) return ROPE_ERR_NULL;
+        if (!p->cos && !gen) return ROPE_ERR_NULL;  // the Rope op needs its tables
     }
-    if ((p->cos == nullptr) != (p->sin == nullptr)) return ROPE_ERR_NULL;
+    if (gen) {
+        if (!p->inv_freq) return ROPE_ERR_NULL;
+        if (!(std::isfinite(p->pos_scale) && p->pos_scale > 0.0f)) return ROPE_ERR_SHAPE;
+        if (p->inv_freq_rows != 1 && p->inv_freq_rows != p->batch) return ROPE_ERR_SHAPE;
+        // rope_qk finds a packed token's sequence by a scan of at most ROPE_MAX_BATCH entries
+        if (!attention && p->cu_seqlens && p->inv_freq_rows > 1 && p->batch > ROPE_MAX_BATCH) return ROPE_ERR_LIMIT;
+        if ((reinterpret_cast<uintptr_t>(p->pos) & 3u) || (reinterpret_cast<uintptr_t>(p->inv_freq) & 3u))
+            return ROPE_ERR_UNSUPPORTED;
+    }
     if (p->batch <= 0 || p->hq <= 0 || p->hkv <= 0 || p->head_dim <= 0) return ROPE_ERR_SHAPE;
     if (p->hq % p->hkv != 0) return ROPE_ERR_SHAPE;
     const bool varlen = p->cu_seqlens != nullptr;
@@ -108,6 +121,7 @@ rope_status check_kv_cache(const rope_kv_cache_params* p) {
     for (unsigned char c : p->rsv)
         if (c) return ROPE_ERR_ABI;
     if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
+    if (!valid_pairing(p->pairing)) return ROPE_ERR_UNSUPPORTED;
     if (p->ntokens < 0 || p->hkv <= 0 || p->head_dim <= 0) return ROPE_ERR_SHAPE;
     // the new tokens' arrays may be NULL when there are none (empty allocations)
     if (p->ntokens > 0 && (!p->k || !p->cos || !p->sin || !p->slots)) return ROPE_ERR_NULL;
@@ -168,6 +182,7 @@ rope_status check_decode(const rope_decode_params* p) {
     if (st != ROPE_OK) return st;
     if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
     if (p->dtype == ROPE_DT_F32) return ROPE_ERR_UNSUPPORTED;
+    if (!valid_pairing(p->pairing)) return ROPE_ERR_UNSUPPORTED;
     if (!p->q || !p->k_cache || !p->v_cache || !p->cache_seqlens || !p->out) return ROPE_ERR_NULL;
     if ((p->cos == nullptr) != (p->sin == nullptr)) return ROPE_ERR_NULL;
     if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f)) return ROPE_ERR_SHAPE;
@@ -250,9 +265,10 @@ rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_len
     return ROPE_OK;
 }
 
-rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
-                        int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype, void* sin_out,
-                        void* cos_out, void* hip_stream) {
+rope_status rope_tables_ex(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
+                           int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype,
+                           rope_pairing pairing, rope_angle_mode angle_mode, void* sin_out, void* cos_out,
+                           void* hip_stream) {
     if (!pos || !inv_freq || !seq_lens || !sin_out || !cos_out) return ROPE_ERR_NULL;
     if (batch <= 0 || ntokens <= 0 || head_size <= 0) return ROPE_ERR_SHAPE;
     if (batch > ROPE_MAX_BATCH || ntokens > ROPE_MAX_NTOKENS) return ROPE_ERR_LIMIT;
@@ -265,11 +281,21 @@ rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t
     if (total != ntokens) return ROPE_ERR_SHAPE;
     if (!(std::isfinite(pos_scale) && pos_scale > 0.0f)) return ROPE_ERR_SHAPE;
     if (!valid_dtype(out_dtype)) return ROPE_ERR_DTYPE;
+    if (!valid_pairing(pairing)) return ROPE_ERR_UNSUPPORTED;
+    if (angle_mode != ROPE_ANGLE_F32 && angle_mode != ROPE_ANGLE_EXACT) return ROPE_ERR_UNSUPPORTED;
     if (!aligned16(inv_freq) || !aligned16(sin_out) || !aligned16(cos_out)) return ROPE_ERR_UNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(pos) & 3u) return ROPE_ERR_UNSUPPORTED;
     const hipError_t e = ropefa::launch_rope_tables(pos, inv_freq, seq_lens, batch, ntokens, head_size, pos_scale,
-                                                    out_dtype, sin_out, cos_out, (hipStream_t)hip_stream);
+                                                    out_dtype, (int)pairing, (int)angle_mode, sin_out, cos_out,
+                                                    (hipStream_t)hip_stream);
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
+                        int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype, void* sin_out,
+                        void* cos_out, void* hip_stream) {
+    return rope_tables_ex(pos, inv_freq, seq_lens, batch, ntokens, head_size, pos_scale, out_dtype, ROPE_PAIR_HALF,
+                          ROPE_ANGLE_F32, sin_out, cos_out, hip_stream);
 }
 
 rope_status rope_qk(const rope_attn_params* p, void* hip_stream) {

@@ -133,13 +133,15 @@ __device__ __forceinline__ void store_chunk<float>(float* p, const Chunk8<float>
 // first half, y the partner columns [j + D/2, j + D/2 + 8); (c0, s0) are the table
 // values of the first-half columns and (c1, s1) of the second-half columns.
 //   x' = x*c0 - y*s0,   y' = y*c1 + x*s1
+// Written as one explicit FMA after one product, so every caller rounds the same way
+// whether its table values were loaded or computed.
 __device__ __forceinline__ void rotate_pair(float (&x)[8], float (&y)[8], const float (&c0)[8], const float (&s0)[8],
                                             const float (&c1)[8], const float (&s1)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float xv = x[e], yv = y[e];
-        x[e] = xv * c0[e] - yv * s0[e];
-        y[e] = yv * c1[e] + xv * s1[e];
+        x[e] = __builtin_fmaf(xv, c0[e], -__fmul_rn(yv, s0[e]));
+        y[e] = __builtin_fmaf(yv, c1[e], __fmul_rn(xv, s1[e]));
     }
 }
 
@@ -163,6 +165,93 @@ __device__ __forceinline__ void rotate_pair_packed(const u32x4& x, const u32x4& 
         xo[i] = Elem<T>::pack(Elem<T>::dot2(xy_e, cs_e, 0.0f), Elem<T>::dot2(xy_o, cs_o, 0.0f));
         yo[i] = Elem<T>::pack(Elem<T>::dot2(xy_e, sc_e, 0.0f), Elem<T>::dot2(xy_o, sc_o, 0.0f));
     }
+}
+
+// ---------------------------------------------------------------- table values
+// Range-reduction constants, derived from pi in extended precision:
+//   kHalfPiHi  = fl32(pi/2),  kHalfPiMid = fl32(pi/2 - kHalfPiHi),
+//   kHalfPiLo  = fl32(pi/2 - kHalfPiHi - kHalfPiMid),  kTwoOverPi = fl32(2/pi).
+// (the host tests recompute them.)
+constexpr float kHalfPiHi = 0x1.921fb6p+0f;
+constexpr float kHalfPiMid = -0x1.777a5cp-25f;
+constexpr float kHalfPiLo = -0x1.ee59dap-50f;
+constexpr float kTwoOverPi = 0x1.45f306p-1f;
+// Arguments up to this magnitude take the fast path below.
+constexpr float kFastPathMax = 1048576.0f;  // 2^20
+
+// sin and cos of a float32 angle.
+//
+// Cody-Waite additive range reduction with fused multiply-adds: k = rint(x * 2/pi),
+// r = x - k*pi/2 with pi/2 split in three float32 parts.  The first FMA is exact for
+// |x| <= 2^20 (x and k*kHalfPiHi are both multiples of 2^-23 there and |r| < 1), the
+// next two add the tail of pi/2, so r keeps nearly full relative precision even close
+// to multiples of pi/2.  On |r| <= pi/4 (plus rounding slack) sin and cos are their
+// Taylor series truncated after r^11 and r^12 (remainders below 3e-9 relative), in
+// Horner form; the quadrant k mod 4 selects and signs the two results.  Larger
+// arguments use the device library's sincosf.
+__device__ __forceinline__ void rope_sincos(float x, float& s, float& c) {
+    if (__builtin_fabsf(x) > kFastPathMax) {
+        sincosf(x, &s, &c);
+        return;
+    }
+    const float k = __builtin_rintf(x * kTwoOverPi);
+    float r = __builtin_fmaf(-k, kHalfPiHi, x);
+    r = __builtin_fmaf(-k, kHalfPiMid, r);
+    r = __builtin_fmaf(-k, kHalfPiLo, r);
+    const float r2 = r * r;
+    // sin r = r + r^3 * (-1/3! + r^2 (1/5! + r^2 (-1/7! + r^2 (1/9! - r^2/11!))))
+    float ps = __builtin_fmaf(r2, -1.0f / 39916800.0f, 1.0f / 362880.0f);
+    ps = __builtin_fmaf(r2, ps, -1.0f / 5040.0f);
+    ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
+    ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
+    const float sr = __builtin_fmaf(r * r2, ps, r);
+    // cos r = 1 + r^2 * (-1/2! + r^2 (1/4! + r^2 (-1/6! + r^2 (1/8! + r^2 (-1/10! + r^2/12!)))))
+    float pc = __builtin_fmaf(r2, 1.0f / 479001600.0f, -1.0f / 3628800.0f);
+    pc = __builtin_fmaf(r2, pc, 1.0f / 40320.0f);
+    pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
+    pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
+    pc = __builtin_fmaf(r2, pc, -0.5f);
+    const float cr = __builtin_fmaf(r2, pc, 1.0f);
+    const int q = ((int)k) & 3;
+    // x = r + q*pi/2:  q=0 (sr, cr)  q=1 (cr, -sr)  q=2 (-sr, -cr)  q=3 (-cr, sr)
+    const float a = (q & 1) ? cr : sr;
+    const float b = (q & 1) ? sr : cr;
+    s = (q & 2) ? -a : a;
+    c = ((q + 1) & 2) ? -b : b;
+}
+
+// The angle of one table entry in float32: fl32(fl32(pos / pos_scale) * inv_freq), each
+// operation correctly rounded and not contracted ([DynamicNTKOperation], 算子功能分析:
+// the outer product of int32 positions with float32 inverse frequencies).
+__device__ __forceinline__ float table_angle(int32_t pos, float pos_scale, float inv_freq) {
+    return __fmul_rn(__fdiv_rn((float)pos, pos_scale), inv_freq);
+}
+
+// Interleaved pairing ([RoPE/GQA tutorial], section 六: adjacent 2-D blocks): elements
+// (2k, 2k+1) of a chunk form one pair, rotated with the table values of their own columns,
+//   x'_2k = x_2k c_2k - x_2k+1 s_2k,   x'_2k+1 = x_2k+1 c_2k+1 + x_2k s_2k+1.
+__device__ __forceinline__ void rotate_interleaved(float (&x)[8], const float (&c)[8], const float (&s)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a = x[2 * k], b = x[2 * k + 1];
+        x[2 * k] = __builtin_fmaf(a, c[2 * k], -__fmul_rn(b, s[2 * k]));
+        x[2 * k + 1] = __builtin_fmaf(b, c[2 * k + 1], __fmul_rn(a, s[2 * k + 1]));
+    }
+}
+
+// The same on packed 16-bit data (4 dwords, one pair per dword): v_perm_b32 builds the
+// (c, -s) and (s, c) operand pairs, v_dot2 the two products in float32; rounded once to T.
+template <typename T>
+__device__ __forceinline__ u32x4 rotate_interleaved_packed(const u32x4& x, const u32x4& c, const u32x4& s) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ns = s[i] ^ 0x80008000u;
+        const uint32_t cs = __builtin_amdgcn_perm(ns, c[i], 0x05040100u);   // (c_2k, -s_2k)
+        const uint32_t sc = __builtin_amdgcn_perm(c[i], s[i], 0x07060302u);  // (s_2k+1, c_2k+1)
+        o[i] = Elem<T>::pack(Elem<T>::dot2(x[i], cs, 0.0f), Elem<T>::dot2(x[i], sc, 0.0f));
+    }
+    return o;
 }
 
 inline int dtype_bytes(rope_dtype dt) {

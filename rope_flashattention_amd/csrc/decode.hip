@@ -1,8 +1,9 @@
 // rope_decode_attn_fwd: one decode step of RoPE + GQA attention over a paged KV cache, gfx950.
 //
 // What is computed: each sequence's new query, rotated with its table row (the rope_qk
-// formula), attends to every key in the sequence's cache ([FlashAttention blog]:
-// Softmax(QK^T/sqrt(d))V; the keys were rotated when they were written).  The g = hq/hkv
+// formula, rotate-half or interleaved pairs), attends to every key in the sequence's
+// cache ([FlashAttention blog]: Softmax(QK^T/sqrt(d))V; the keys were rotated when they
+// were written).  The g = hq/hkv
 // query heads that share a kv head ([RoPE/GQA tutorial], sections 十一-十二) are served by
 // one pass over that head's cache, so the cache is read once per kv head, which is the
 // traffic GQA exists to save.  A decode step does a few flops per cached byte, so the
@@ -53,6 +54,7 @@ struct DecodeArgs {
     int32_t block_size, max_blocks, num_blocks, max_seqlen;
     float scale_log2;
     int32_t rotate;
+    int32_t interleaved;  // query pairing: 0 rotate-half, 1 interleaved
     int32_t chunk;      // keys per split (multiple of 32)
     int32_t bs_shift;   // log2(block_size) when it is a power of two, else -1
     int32_t table_regs; // 1: a split's block-table entries fit one register per lane
@@ -158,7 +160,12 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
                 unpack<T>(load_chunk<T>(srow + d), s0);
                 unpack<T>(load_chunk<T>(crow + d + D / 2), c1);
                 unpack<T>(load_chunk<T>(srow + d + D / 2), s1);
-                rotate_pair(x, y, c0, s0, c1, s1);
+                if (a.interleaved) {
+                    rotate_interleaved(x, c0, s0);
+                    rotate_interleaved(y, c1, s1);
+                } else {
+                    rotate_pair(x, y, c0, s0, c1, s1);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -361,6 +368,7 @@ hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream) {
     a.cos = p->cos;
     a.sin = p->sin;
     a.rotate = p->cos != nullptr;
+    a.interleaved = p->pairing == ROPE_PAIR_INTERLEAVED;
     a.kc = p->k_cache;
     a.vc = p->v_cache;
     a.block_table = p->block_table;

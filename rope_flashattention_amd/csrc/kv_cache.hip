@@ -1,5 +1,5 @@
-// rope_kv_rms_norm_rope_cache: RMSNorm + rotate-half RoPE of new K rows, written with V
-// into a (possibly paged) KV cache, on gfx950.
+// rope_kv_rms_norm_rope_cache: RMSNorm + RoPE (rotate-half or interleaved pairs) of new K
+// rows, written with V into a (possibly paged) KV cache, on gfx950.
 //
 // The [RoPE-fusion blog] (section 五) names this fused step, the one that runs before
 // attention; the RMSNorm is the [RoPE/GQA tutorial]'s (section 八): scale a head row by the
@@ -9,8 +9,9 @@
 // heads of a token and stay in the caches.
 //
 // Thread mapping: a group of G lanes (G a power of two dividing the wavefront) owns one
-// (token, head) row; lane l owns the chunk pairs (c, c + D/2) with c = l + p*G, 8 columns
-// each, so every rotation pair lives in one thread.  Every load of a thread is issued
+// (token, head) row; lane l owns the chunks c and c + D/2 with c = l + p*G, 8 columns
+// each, so every rotation pair lives in one thread (rotate-half: the two chunks are
+// partners; interleaved: each chunk holds whole pairs).  Every load of a thread is issued
 // before any arithmetic (more bytes in flight per lane), V is stored straight away, then
 // the sum of squares is reduced across the group with xor shuffles.  A whole group leaves
 // together (row past the end, or a skipped slot), so every shuffle partner is live.
@@ -36,6 +37,7 @@ struct KvCacheArgs {
     int32_t block_size;
     float eps;
     int32_t group;           // lanes per row, power of two <= 64
+    int32_t interleaved;     // pairing: 0 rotate-half, 1 interleaved
 };
 
 // Streaming loads of K and V: each byte is read once, so they are marked nontemporal and
@@ -143,7 +145,12 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
             unpack<T>(sx[p], s0);
             unpack<T>(cy[p], c1);
             unpack<T>(sy[p], s1);
-            rotate_pair(x[p], y[p], c0, s0, c1, s1);
+            if (a.interleaved) {
+                rotate_interleaved(x[p], c0, s0);
+                rotate_interleaved(y[p], c1, s1);
+            } else {
+                rotate_pair(x[p], y[p], c0, s0, c1, s1);
+            }
             store_chunk<T>(kdst + c * 8, pack<T>(x[p]));
             store_chunk<T>(kdst + c * 8 + half, pack<T>(y[p]));
         }
@@ -182,6 +189,7 @@ hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream) {
     a.head_dim = p->head_dim;
     a.block_size = p->block_size;
     a.eps = p->eps;
+    a.interleaved = p->pairing == ROPE_PAIR_INTERLEAVED;
     // chunk pairs per row: head_dim / 16 (2..128); lanes per row: that rounded up to a
     // power of two, at most one wavefront; two pairs per lane above 64 pairs
     const int pairs = p->head_dim / 16;

@@ -6,64 +6,14 @@
 // Linear position scaling ([RoPE-fusion blog], section 5.3) divides positions first.
 //
 // One thread owns one token and 8 consecutive frequencies i .. i+7: it computes 8
-// sin/cos pairs once and stores each pair of 8 results twice (columns i and i + D/2),
-// so every transcendental evaluation feeds four stores.  The kernel is bound by HBM
-// writes (2 * ntokens * D * sizeof(out)).
+// sin/cos pairs once and stores each result twice (columns i and i + D/2 for the
+// rotate-half layout, 2i and 2i + 1 for the interleaved one), so every transcendental
+// evaluation feeds four stores.  The kernel is bound by HBM writes
+// (2 * ntokens * D * sizeof(out)).  The exact-angle mode forms angles and sin/cos in
+// float64 and rounds each value once to the output type.
 #include "common.h"
 
 namespace ropefa {
-
-// Range-reduction constants, derived from pi in extended precision:
-//   kHalfPiHi  = fl32(pi/2),  kHalfPiMid = fl32(pi/2 - kHalfPiHi),
-//   kHalfPiLo  = fl32(pi/2 - kHalfPiHi - kHalfPiMid),  kTwoOverPi = fl32(2/pi).
-// (tests/test_host.py recomputes them.)
-constexpr float kHalfPiHi = 0x1.921fb6p+0f;
-constexpr float kHalfPiMid = -0x1.777a5cp-25f;
-constexpr float kHalfPiLo = -0x1.ee59dap-50f;
-constexpr float kTwoOverPi = 0x1.45f306p-1f;
-// Arguments up to this magnitude take the fast path below.
-constexpr float kFastPathMax = 1048576.0f;  // 2^20
-
-// sin and cos of a float32 angle.
-//
-// Cody-Waite additive range reduction with fused multiply-adds: k = rint(x * 2/pi),
-// r = x - k*pi/2 with pi/2 split in three float32 parts.  The first FMA is exact for
-// |x| <= 2^20 (x and k*kHalfPiHi are both multiples of 2^-23 there and |r| < 1), the
-// next two add the tail of pi/2, so r keeps nearly full relative precision even close
-// to multiples of pi/2.  On |r| <= pi/4 (plus rounding slack) sin and cos are their
-// Taylor series truncated after r^11 and r^12 (remainders below 3e-9 relative), in
-// Horner form; the quadrant k mod 4 selects and signs the two results.  Larger
-// arguments use the device library's sincosf.
-__device__ __forceinline__ void rope_sincos(float x, float& s, float& c) {
-    if (__builtin_fabsf(x) > kFastPathMax) {
-        sincosf(x, &s, &c);
-        return;
-    }
-    const float k = __builtin_rintf(x * kTwoOverPi);
-    float r = __builtin_fmaf(-k, kHalfPiHi, x);
-    r = __builtin_fmaf(-k, kHalfPiMid, r);
-    r = __builtin_fmaf(-k, kHalfPiLo, r);
-    const float r2 = r * r;
-    // sin r = r + r^3 * (-1/3! + r^2 (1/5! + r^2 (-1/7! + r^2 (1/9! - r^2/11!))))
-    float ps = __builtin_fmaf(r2, -1.0f / 39916800.0f, 1.0f / 362880.0f);
-    ps = __builtin_fmaf(r2, ps, -1.0f / 5040.0f);
-    ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
-    ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
-    const float sr = __builtin_fmaf(r * r2, ps, r);
-    // cos r = 1 + r^2 * (-1/2! + r^2 (1/4! + r^2 (-1/6! + r^2 (1/8! + r^2 (-1/10! + r^2/12!)))))
-    float pc = __builtin_fmaf(r2, 1.0f / 479001600.0f, -1.0f / 3628800.0f);
-    pc = __builtin_fmaf(r2, pc, 1.0f / 40320.0f);
-    pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
-    pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
-    pc = __builtin_fmaf(r2, pc, -0.5f);
-    const float cr = __builtin_fmaf(r2, pc, 1.0f);
-    const int q = ((int)k) & 3;
-    // x = r + q*pi/2:  q=0 (sr, cr)  q=1 (cr, -sr)  q=2 (-sr, -cr)  q=3 (-cr, sr)
-    const float a = (q & 1) ? cr : sr;
-    const float b = (q & 1) ? sr : cr;
-    s = (q & 2) ? -a : a;
-    c = ((q + 1) & 2) ? -b : b;
-}
 
 struct TablesArgs {
     const int32_t* pos;
@@ -77,7 +27,16 @@ struct TablesArgs {
     int32_t starts[ROPE_MAX_BATCH + 1];  // exclusive prefix sums of seq_lens
 };
 
-template <typename TO>
+// float64 -> float32 rounded to odd (truncate, then set the last bit if anything was cut):
+// a later round-to-nearest-even to bf16 or fp16 (at least 2 fewer bits) then rounds the
+// float64 value correctly, with no double-rounding error.
+__device__ __forceinline__ float round_to_odd_f32(double d) {
+    const float t = __double2float_rz(d);
+    const uint32_t u = __float_as_uint(t) | ((double)t != d ? 1u : 0u);
+    return __uint_as_float(u);
+}
+
+template <typename TO, int PAIR, bool EXACT>
 __global__ __launch_bounds__(256) void rope_tables_kernel(TablesArgs a) {
     const int half = a.head_size >> 1;
     const int chunks = half >> 3;  // 8-frequency chunks per row
@@ -88,30 +47,68 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(TablesArgs a) {
     int b = 0;
 #pragma unroll
     for (int i = 1; i < ROPE_MAX_BATCH; ++i) b += (i < a.batch && t >= a.starts[i]) ? 1 : 0;
-    // fl32(pos / s): a correctly rounded division
-    const float p = __fdiv_rn((float)a.pos[t], a.pos_scale);
     const float* f = a.inv_freq + (int64_t)b * half + j;
     const f32x4 f0 = *reinterpret_cast<const f32x4*>(f);
     const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + 4);
     float sv[8], cv[8];
+    if (EXACT) {
+        const double p = (double)a.pos[t] / (double)a.pos_scale;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float fe = e < 4 ? f0[e] : f1[e - 4];
-        rope_sincos(__fmul_rn(p, fe), sv[e], cv[e]);  // fl32(p * f), no contraction
+        for (int e = 0; e < 8; ++e) {
+            double sd, cd;
+            sincos(p * (double)(e < 4 ? f0[e] : f1[e - 4]), &sd, &cd);
+            if (sizeof(TO) == 4) {
+                sv[e] = (float)sd;
+                cv[e] = (float)cd;
+            } else {
+                sv[e] = round_to_odd_f32(sd);
+                cv[e] = round_to_odd_f32(cd);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rope_sincos(table_angle(a.pos[t], a.pos_scale, e < 4 ? f0[e] : f1[e - 4]), sv[e], cv[e]);
     }
-    const Chunk8<TO> sc = pack<TO>(sv);
-    const Chunk8<TO> cc = pack<TO>(cv);
-    TO* so = reinterpret_cast<TO*>(a.sin_out) + (int64_t)t * a.head_size + j;
-    TO* co = reinterpret_cast<TO*>(a.cos_out) + (int64_t)t * a.head_size + j;
-    store_chunk<TO>(so, sc);
-    store_chunk<TO>(so + half, sc);
-    store_chunk<TO>(co, cc);
-    store_chunk<TO>(co + half, cc);
+    TO* so = reinterpret_cast<TO*>(a.sin_out) + (int64_t)t * a.head_size;
+    TO* co = reinterpret_cast<TO*>(a.cos_out) + (int64_t)t * a.head_size;
+    if (PAIR == ROPE_PAIR_HALF) {
+        // frequency i fills columns i and i + D/2
+        const Chunk8<TO> sc = pack<TO>(sv);
+        const Chunk8<TO> cc = pack<TO>(cv);
+        store_chunk<TO>(so + j, sc);
+        store_chunk<TO>(so + j + half, sc);
+        store_chunk<TO>(co + j, cc);
+        store_chunk<TO>(co + j + half, cc);
+    } else {
+        // frequency i fills columns 2i and 2i + 1
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            float s2[8], c2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s2[e] = sv[4 * hlf + e / 2];
+                c2[e] = cv[4 * hlf + e / 2];
+            }
+            store_chunk<TO>(so + 2 * j + 8 * hlf, pack<TO>(s2));
+            store_chunk<TO>(co + 2 * j + 8 * hlf, pack<TO>(c2));
+        }
+    }
+}
+
+template <typename TO>
+static void launch_tables_typed(const TablesArgs& a, int pairing, int angle_mode, dim3 grid, hipStream_t stream) {
+    const int key = pairing * 2 + angle_mode;
+    switch (key) {
+        case 0: hipLaunchKernelGGL((rope_tables_kernel<TO, ROPE_PAIR_HALF, false>), grid, dim3(256), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((rope_tables_kernel<TO, ROPE_PAIR_HALF, true>), grid, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rope_tables_kernel<TO, ROPE_PAIR_INTERLEAVED, false>), grid, dim3(256), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rope_tables_kernel<TO, ROPE_PAIR_INTERLEAVED, true>), grid, dim3(256), 0, stream, a); break;
+    }
 }
 
 hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const int32_t* seq_lens, int32_t batch,
                               int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype,
-                              void* sin_out, void* cos_out, hipStream_t stream) {
+                              int pairing, int angle_mode, void* sin_out, void* cos_out, hipStream_t stream) {
     TablesArgs a;
     a.pos = pos;
     a.inv_freq = inv_freq;
@@ -124,12 +121,11 @@ hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const i
     a.starts[0] = 0;
     for (int i = 0; i < ROPE_MAX_BATCH; ++i) a.starts[i + 1] = a.starts[i] + (i < batch ? seq_lens[i] : 0);
     const int64_t threads = (int64_t)ntokens * (head_size / 16);
-    const dim3 block(256);
     const dim3 grid((unsigned)((threads + 255) / 256));
     switch (out_dtype) {
-        case ROPE_DT_BF16: hipLaunchKernelGGL(rope_tables_kernel<__bf16>, grid, block, 0, stream, a); break;
-        case ROPE_DT_F16: hipLaunchKernelGGL(rope_tables_kernel<_Float16>, grid, block, 0, stream, a); break;
-        case ROPE_DT_F32: hipLaunchKernelGGL(rope_tables_kernel<float>, grid, block, 0, stream, a); break;
+        case ROPE_DT_BF16: launch_tables_typed<__bf16>(a, pairing, angle_mode, grid, stream); break;
+        case ROPE_DT_F16: launch_tables_typed<_Float16>(a, pairing, angle_mode, grid, stream); break;
+        case ROPE_DT_F32: launch_tables_typed<float>(a, pairing, angle_mode, grid, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(ropelib):
 
 
 def test_abi_version_and_struct_size(ropelib):
-    assert ropelib.rope_abi_version() == 1
+    assert ropelib.rope_abi_version() == 2
     assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
     assert ropelib.rope_kv_cache_params_size() == ctypes.sizeof(RopeKvCacheParams)
     assert ropelib.rope_decode_params_size() == ctypes.sizeof(RopeDecodeParams)
@@ -210,6 +210,54 @@ def test_rope_qk_rejects(ropelib, kw, status):
 
 
 @no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(pairing=2), "ROPE_ERR_UNSUPPORTED"),
+    (dict(cos=None, sin=None, pos=FAKE), "ROPE_ERR_NULL"),                       # formed tables need inv_freq
+    (dict(cos=None, sin=None, pos=FAKE, inv_freq=FAKE, inv_freq_rows=1, pos_scale=0.0), "ROPE_ERR_SHAPE"),
+    (dict(cos=None, sin=None, pos=FAKE, inv_freq=FAKE, inv_freq_rows=3, pos_scale=1.0), "ROPE_ERR_SHAPE"),
+    (dict(cos=None, sin=None, pos=FAKE + 2, inv_freq=FAKE, inv_freq_rows=1, pos_scale=1.0), "ROPE_ERR_UNSUPPORTED"),
+    (dict(cos=None, sin=None, pos=FAKE, inv_freq=FAKE + 2, inv_freq_rows=1, pos_scale=1.0),
+     "ROPE_ERR_UNSUPPORTED"),
+])
+def test_formed_tables_and_pairing_rejects(ropelib, kw, status):
+    for attention in (True, False):
+        p = mutate(valid_params(attention=attention), **kw)
+        fn = ropelib.rope_flash_attn_fwd if attention else ropelib.rope_qk
+        assert fn(ctypes.byref(p), None) == ST[status]
+
+
+@no_gpu_only
+def test_rope_qk_varlen_per_sequence_freqs_limit(ropelib):
+    # rope_qk finds a packed token's sequence among at most ROPE_MAX_BATCH entries
+    p = mutate(valid_params(attention=False, B=17), cos=None, sin=None, pos=FAKE, inv_freq=FAKE, inv_freq_rows=17,
+               pos_scale=1.0, cu_seqlens=FAKE, max_seqlen=100, ntokens=1700)
+    p.q_stride[:] = p.k_stride[:] = (0, 8 * 128, 128, 1)
+    assert ropelib.rope_qk(ctypes.byref(p), None) == ST["ROPE_ERR_LIMIT"]
+
+
+@no_gpu_only
+def test_tables_ex_rejects(ropelib):
+    lens = np.array([4, 4], dtype=np.int32)
+    def call(pairing, mode):
+        return ropelib.rope_tables_ex(FAKE, FAKE, lens.ctypes.data, 2, 8, 128, 1.0, 2, pairing, mode, FAKE, FAKE,
+                                      None)
+    assert call(2, 0) == ST["ROPE_ERR_UNSUPPORTED"]
+    assert call(0, 2) == ST["ROPE_ERR_UNSUPPORTED"]
+    assert call(-1, 0) == ST["ROPE_ERR_UNSUPPORTED"]
+    # the other checks are rope_tables' own
+    assert ropelib.rope_tables_ex(FAKE, FAKE, lens.ctypes.data, 2, 9, 128, 1.0, 2, 1, 1, FAKE, FAKE, None) == \
+        ST["ROPE_ERR_SHAPE"]
+
+
+@no_gpu_only
+def test_cache_and_decode_pairing_rejects(ropelib):
+    p = mutate(valid_cache_params(), pairing=2)
+    assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+    p = mutate(valid_decode_params(), pairing=5)
+    assert ropelib.rope_decode_attn_fwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+
+
+@no_gpu_only
 def test_null_params(ropelib):
     assert ropelib.rope_qk(None, None) == ST["ROPE_ERR_NULL"]
     assert ropelib.rope_flash_attn_fwd(None, None) == ST["ROPE_ERR_NULL"]
@@ -357,7 +405,7 @@ def test_binding_refuses_cpu_tensors(ropelib):
 def test_sincos_constants_derive_from_pi():
     mpmath = pytest.importorskip("mpmath")
     mpmath.mp.dps = 60
-    src = open(os.path.join(ROOT, "rope_flashattention_amd", "csrc", "rope_tables.hip")).read()
+    src = open(os.path.join(ROOT, "rope_flashattention_amd", "csrc", "common.h")).read()
 
     def const(name):
         m = re.search(r"constexpr float %s = ([-0-9a-fx.p+]+)f;" % name, src)
