@@ -60,6 +60,8 @@ __all__ = [
     "decode_attention",
     "pair_partner",
     "PAIRINGS",
+    "rotate_tokens_transpose",
+    "rope_attention_bwd",
 ]
 
 PAIRINGS = ("half", "interleaved")
@@ -353,6 +355,64 @@ def rope_attention_rows(q, k, v, cos, sin, seq_lens, scale: float, causal: bool,
         outs.append((e / l) @ vv[:n_keys])
         lses.append(m + np.log(l))
     return np.stack(outs), np.asarray(lses)
+
+
+# --------------------------------------------------------------------------- backward
+def rotate_tokens_transpose(g, cos, sin, pairing: str = "half") -> np.ndarray:
+    """Apply the transpose of each token's Rope-op matrix to g [T, H, D] (float64 out).
+
+    The forward maps x to M_t x (``rope_op_matrix``); the gradient with respect to x of a
+    function of M_t x is M_t^T times its gradient with respect to M_t x.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    out = np.empty_like(g)
+    for t in range(g.shape[0]):
+        M = rope_op_matrix(cos[t], sin[t], pairing)
+        out[t] = g[t] @ M          # row vectors: (M^T g^T)^T = g M
+    return out
+
+
+def rope_attention_bwd(q, k, v, dout, cos, sin, seq_lens, scale: float, causal: bool = True,
+                       pairing: str = "half"):
+    """Gradients (dq, dk, dv) of sum(O * dout) for O = rope_attention(q, k, v, ...).
+
+    The pages say the operator serves training ([FlashAttention blog]) without writing the
+    backward out; these are the derivatives of the forward definition, in the usual
+    three-matrix form per (sequence, q head): with P the row softmax of S = scale * q' k'^T,
+      dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dP * P)),
+      dq' = scale * dS k',   dk' = scale * dS^T q',
+    then dq = M^T dq' and dk = M^T dk' through each token's Rope-op matrix M.  GQA: the
+    gradients of a kv head sum over the q heads of its group.  Float64 throughout.
+    """
+    T, Hq, Hkv, D = _check_packed(q, k, v, seq_lens)
+    g = Hq // Hkv
+    dout = np.asarray(dout, dtype=np.float64)
+    qr = rotate_tokens(q, cos, sin, pairing=pairing)
+    kr = rotate_tokens(k, cos, sin, pairing=pairing)
+    v = np.asarray(v, dtype=np.float64)
+    dqr = np.zeros((T, Hq, D))
+    dkr = np.zeros((T, Hkv, D))
+    dv = np.zeros((T, Hkv, D))
+    for s0, L in zip(segment_starts(seq_lens).tolist(), np.asarray(seq_lens).tolist()):
+        sl = slice(s0, s0 + L)
+        for h in range(Hq):
+            kvh = h // g
+            S = (qr[sl, h] @ kr[sl, kvh].T) * float(scale)
+            if causal:
+                S = np.where(np.tril(np.ones((L, L), dtype=bool)), S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dO = dout[sl, h]
+            dv[sl, kvh] += P.T @ dO
+            dP = dO @ v[sl, kvh].T
+            dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+            dqr[sl, h] = float(scale) * dS @ kr[sl, kvh]
+            dkr[sl, kvh] += float(scale) * dS.T @ qr[sl, h]
+    dq = rotate_tokens_transpose(dqr, cos, sin, pairing)
+    dk = rotate_tokens_transpose(dkr, cos, sin, pairing)
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------- KV-cache step

@@ -584,6 +584,64 @@ def test_decode_attention():
     check_decode(orc.decode_attention, orc.cache_slots)
 
 
+# --------------------------------------------------------------------------- backward
+def _fd_loss(q, k, v, dout, cos, sin, seq_lens, scale, causal, pairing):
+    o, _ = orc.rope_attention(q, k, v, cos, sin, seq_lens, scale, causal, pairing)
+    return float(np.sum(o * dout))
+
+
+def check_backward(rope_attention_bwd):
+    """Directional derivatives of the (pinned) forward by central differences."""
+    r = rng(14)
+    for seq_lens, Hq, Hkv, causal, pairing, tables in (([7], 2, 1, True, "half", "rotation"),
+                                                       ([4, 5], 4, 2, True, "interleaved", "rotation"),
+                                                       ([6], 2, 2, False, "half", "random")):
+        T, D = sum(seq_lens), 8
+        q = r.standard_normal((T, Hq, D))
+        k = r.standard_normal((T, Hkv, D))
+        v = r.standard_normal((T, Hkv, D))
+        dout = r.standard_normal((T, Hq, D))
+        if tables == "rotation":
+            theta = r.uniform(-3, 3, size=(T, D // 2))
+            cols = orc.pair_partner(D, pairing)[2]
+            cos, sin = np.cos(theta[:, cols]), np.sin(theta[:, cols])
+        else:   # arbitrary table values: the Rope op is then a general linear map
+            cos, sin = r.uniform(-1, 1, (T, D)), r.uniform(-1, 1, (T, D))
+        scale = 0.6
+        dq, dk, dv = rope_attention_bwd(q, k, v, dout, cos, sin, seq_lens, scale, causal, pairing)
+        eps = 1e-5
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            u = r.standard_normal(x.shape)
+            args = dict(q=q, k=k, v=v)
+            args[name] = x + eps * u
+            lp = _fd_loss(args["q"], args["k"], args["v"], dout, cos, sin, seq_lens, scale, causal, pairing)
+            args[name] = x - eps * u
+            lm = _fd_loss(args["q"], args["k"], args["v"], dout, cos, sin, seq_lens, scale, causal, pairing)
+            fd = (lp - lm) / (2 * eps)
+            an = float(np.sum(grad * u))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, seq_lens, pairing, tables, fd, an)
+
+
+def test_backward_finite_differences():
+    check_backward(orc.rope_attention_bwd)
+
+
+def test_backward_segments_do_not_mix():
+    # the gradient of one sequence's keys ignores another sequence's output gradient
+    r = rng(15)
+    T, H, D = 9, 2, 8
+    q, k, v = (r.standard_normal((T, H, D)) for _ in range(3))
+    theta = r.uniform(-3, 3, size=(T, D // 2))
+    cos, sin = np.cos(np.concatenate([theta, theta], 1)), np.sin(np.concatenate([theta, theta], 1))
+    dout = r.standard_normal((T, H, D))
+    dout2 = dout.copy()
+    dout2[:4] = r.standard_normal((4, H, D))   # change the first sequence only
+    a = orc.rope_attention_bwd(q, k, v, dout, cos, sin, [4, 5], 0.5)
+    b = orc.rope_attention_bwd(q, k, v, dout2, cos, sin, [4, 5], 0.5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x[4:], y[4:]) and not np.array_equal(x[:4], y[:4])
+
+
 # --------------------------------------------------------------------------- planted mistakes
 # Each mutant is one plausible slip; at least one pin above must reject it.
 
@@ -721,6 +779,51 @@ def _mut_rotate_tokens_interleaved_swapped(x, cos, sin, chunk=512, pairing="half
     return x * np.asarray(cos)[:, None, :] + sign * x[..., partner] * np.asarray(sin)[:, None, :]
 
 
+def _mut_bwd_no_transpose(q, k, v, dout, cos, sin, seq_lens, scale, causal=True, pairing="half"):
+    # rotates the gradients forward instead of applying M^T
+    dq, dk, dv = orc.rope_attention_bwd(q, k, v, dout, cos, sin, seq_lens, scale, causal, pairing)
+    back = lambda g: orc.rotate_tokens(orc.rotate_tokens(g, cos, sin, pairing=pairing), cos, sin, pairing=pairing)
+    return back(dq), back(dk), dv
+
+
+def _mut_bwd_no_rowsum(q, k, v, dout, cos, sin, seq_lens, scale, causal=True, pairing="half"):
+    T, Hq, D = np.asarray(q).shape
+    Hkv = np.asarray(k).shape[1]
+    qr = orc.rotate_tokens(q, cos, sin, pairing=pairing)
+    kr = orc.rotate_tokens(k, cos, sin, pairing=pairing)
+    dq, dk, dv = orc.rope_attention_bwd(q, k, v, dout, cos, sin, seq_lens, scale, causal, pairing)
+    # recompute dq without the rowsum term
+    g = Hq // Hkv
+    dqr = np.zeros((T, Hq, D))
+    for s0, L in zip(orc.segment_starts(seq_lens).tolist(), list(seq_lens)):
+        sl = slice(s0, s0 + L)
+        for h in range(Hq):
+            S = (qr[sl, h] @ kr[sl, h // g].T) * scale
+            if causal:
+                S = np.where(np.tril(np.ones((L, L), dtype=bool)), S, -np.inf)
+            P = np.exp(S - S.max(1, keepdims=True))
+            P /= P.sum(1, keepdims=True)
+            dS = P * (np.asarray(dout)[sl, h] @ np.asarray(v)[sl, h // g].T)
+            dqr[sl, h] = scale * dS @ kr[sl, h // g]
+    return orc.rotate_tokens_transpose(dqr, cos, sin, pairing), dk, dv
+
+
+def _mut_bwd_gqa_first_head(q, k, v, dout, cos, sin, seq_lens, scale, causal=True, pairing="half"):
+    # dk, dv from the first q head of each group only
+    q = np.asarray(q)
+    Hq, Hkv = q.shape[1], np.asarray(k).shape[1]
+    g = Hq // Hkv
+    dq, dk, dv = orc.rope_attention_bwd(q, k, v, dout, cos, sin, seq_lens, scale, causal, pairing)
+    if g == 1:
+        return dq, dk, dv
+    d2 = np.array(dout, dtype=np.float64)
+    for h in range(Hq):
+        if h % g:
+            d2[:, h] = 0.0
+    _, dk1, dv1 = orc.rope_attention_bwd(q, k, v, d2, cos, sin, seq_lens, scale, causal, pairing)
+    return dq, dk1, dv1
+
+
 def _mut_rope_attention_gqa_strided(q, k, v, cos, sin, seq_lens, scale, causal=True):
     hq, hkv = q.shape[1], k.shape[1]
     idx = np.arange(hq) % hkv                      # strided instead of contiguous groups
@@ -761,6 +864,9 @@ def _mut_rope_attention_no_segments(q, k, v, cos, sin, seq_lens, scale, causal=T
     ("interleaved partner two away", lambda g: check_interleaved(orc.rotation_matrix, orc.rope_op_matrix,
                                                                  _mut_rotate_tokens_interleaved_swapped,
                                                                  orc.rope_tables)),
+    ("backward without the transpose", lambda g: check_backward(_mut_bwd_no_transpose)),
+    ("backward without the rowsum", lambda g: check_backward(_mut_bwd_no_rowsum)),
+    ("backward GQA from one head", lambda g: check_backward(_mut_bwd_gqa_first_head)),
 ])
 def test_pins_reject_planted_mistakes(name, run, golden_dir):
     with open(os.path.join(golden_dir, "dynamic_ntk_tiny.json")) as fh:
