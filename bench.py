@@ -13,8 +13,9 @@ steps.  The roofline object reports the attention kernel's own time, measured wi
 events on the stream it runs on, against the dense bf16 MFMA peak.  Extra measurements
 (after the timed region): rope_tables GB/s at the op's size limits, rope_qk GB/s on the
 workload, the unfused path (rope_qk + attention without rotation) for the fusion
-ablation, the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill, and
-decode-step attention GB/s over a paged cache.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
+ablation, the RoPE variants of the fused kernel, the backward pass, the fused RMSNorm +
+RoPE + KV-cache write GB/s on a paged-cache prefill, and decode-step attention GB/s over a
+paged cache.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
 """
 
 import argparse
@@ -253,6 +254,23 @@ def main():
         comp["unfused_ms"] = round(ms + ms_plain, 4)
         comp["fused_ms"] = round(att_ms, 4)
         del oq, ok
+        # backward on the same workload (delta, dk/dv and dq kernels; dO seeded): algorithmic
+        # FLOPs 2.5x the forward's (the five products S, dP, dV, dK, dQ; the dq kernel's
+        # recomputation of S and dP is overhead, not counted)
+        if w.dtype != "f32":
+            out_f, lse_f = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
+                                                   return_lse=True, **akw)
+            bdo = wl.generate_dout(inp, 9001).to(dev)
+            if not w.varlen and akw.get("layout") == "BSND":
+                bdo = bdo.transpose(1, 2).contiguous()
+            bdq, bdk, bdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            bfn = lambda: rfa.rope_flash_attn_bwd(q, k, v, out_f, lse_f, bdo, cos, sin, causal=w.causal,
+                                                  softmax_scale=w.softmax_scale, dq=bdq, dk=bdk, dv=bdv, **akw)
+            bfn()
+            bms = time_events(bfn, 10, torch)
+            comp["bwd_ms"] = round(bms, 4)
+            comp["bwd_tflops"] = round(2.5 * flops / (bms * 1e-3) / 1e12, 2)
+            del out_f, lse_f, bdo, bdq, bdk, bdv
         # RoPE variants of the fused kernel on the same workload: interleaved pairs (tables
         # from rope_tables_ex), and table values formed inside the kernel (no table read, no
         # table pass) for both pairings

@@ -250,6 +250,56 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
 rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream);
 
 /*
+ * Parameters of rope_flash_attn_bwd: the forward call's parameters plus the gradients.
+ *
+ * fwd.out must hold the forward output O and fwd.lse its lse (both from the forward call
+ * with the same inputs; lse is required here).  Rotation: tables (fwd.cos, fwd.sin, with
+ * fwd.pairing) or none (both NULL); tables formed in the kernel (fwd.pos) are not served
+ * by the backward (ROPE_ERR_UNSUPPORTED).  dout, dq have hq heads, dk, dv hkv heads; strides
+ * {batch, token, head, dim} as for the forward tensors (dim stride 1).  dq, dk, dv are
+ * written in full (every element of every valid token) and must not overlap the inputs.
+ */
+typedef struct rope_attn_bwd_params {
+    uint32_t struct_size;       /* = sizeof(rope_attn_bwd_params), else ROPE_ERR_ABI */
+    rope_attn_params fwd;       /* the forward parameters (fwd.struct_size checked too) */
+    const void* dout;           /* DEVICE gradient of the output, like fwd.out */
+    void* dq;                   /* DEVICE, like q */
+    void* dk;                   /* DEVICE, like k */
+    void* dv;                   /* DEVICE, like v */
+    int64_t do_stride[4];       /* {batch, token, head, dim} in elements */
+    int64_t dq_stride[4];
+    int64_t dk_stride[4];
+    int64_t dv_stride[4];
+    void* workspace;            /* DEVICE scratch, 256-byte aligned, >= rope_flash_attn_bwd_workspace_size() */
+    uint64_t workspace_bytes;
+    uint8_t rsv[16];            /* reserved, must be zero */
+} rope_attn_bwd_params;
+
+/* Workspace bytes rope_flash_attn_bwd needs (one float per query row and q head), or 0
+ * when the shapes are invalid.  Host only. */
+uint64_t rope_flash_attn_bwd_workspace_size(const rope_attn_bwd_params* p);
+
+/*
+ * rope_flash_attn_bwd — gradients of rope_flash_attn_fwd: with the forward's
+ * O = softmax(s * q'k'^T) V per (sequence, q head) (s = softmax_scale, q' and k' the rotated
+ * rows), and dO the gradient of O,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dq' = s * dS k',  dk' = s * dS^T q',  dq = M^T dq',  dk = M^T dk'
+ * with M each token's Rope-op matrix (its transpose undoes the rotation), and the dk, dv of
+ * a kv head summed over the q heads of its group ([RoPE/GQA tutorial], sections 十一-十二).
+ * The [FlashAttention blog] states that the operator serves training; the gradients are
+ * those of the forward definition.  P is recomputed from the forward's lse, never stored.
+ * Supported: F16/BF16, head_dim 64 or 128, causal or not, dense or varlen, GQA, both
+ * pairings.  float32 accumulation; outputs rounded once to dtype.
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, WORKSPACE, HIP.  Three kernel launches
+ * (row deltas, dk/dv, dq).
+ */
+rope_status rope_flash_attn_bwd(const rope_attn_bwd_params* p, void* hip_stream);
+
+/* sizeof(rope_attn_bwd_params) as compiled into the library (for bindings to check). */
+uint32_t rope_attn_bwd_params_size(void);
+
+/*
  * Parameters of rope_kv_rms_norm_rope_cache.
  *
  * New tokens are rows t < ntokens of k and v: head h of token t lives at

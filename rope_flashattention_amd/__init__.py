@@ -6,7 +6,8 @@ in the library's HIP kernels.  There is no fallback: if the library is missing o
 call is rejected, an exception is raised.
 
 Names follow the C ABI: ``inv_freq`` (rope_inv_freq), ``rope_tables``, ``rope_qk``,
-``rope_flash_attn_fwd``, ``rope_kv_rms_norm_rope_cache``, ``rope_decode_attn_fwd``.
+``rope_flash_attn_fwd``, ``rope_flash_attn_bwd``, ``rope_kv_rms_norm_rope_cache``,
+``rope_decode_attn_fwd``.
 """
 
 from __future__ import annotations
@@ -25,12 +26,14 @@ __all__ = [
     "rope_tables",
     "rope_qk",
     "rope_flash_attn_fwd",
+    "rope_flash_attn_bwd",
     "rope_kv_rms_norm_rope_cache",
     "rope_decode_attn_fwd",
     "decode_workspace_size",
     "RopeAttnParams",
     "RopeKvCacheParams",
     "RopeDecodeParams",
+    "RopeAttnBwdParams",
     "STATUS",
     "DTYPE",
     "PAIRING",
@@ -91,6 +94,26 @@ class RopeAttnParams(ctypes.Structure):
         ("inv_freq", ctypes.c_void_p),
         ("inv_freq_rows", ctypes.c_int32),
         ("pos_scale", ctypes.c_float),
+        ("rsv", ctypes.c_uint8 * 16),
+    ]
+
+
+class RopeAttnBwdParams(ctypes.Structure):
+    """Mirror of ``rope_attn_bwd_params`` in include/rope_fa.h (checked against the library's size)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("fwd", RopeAttnParams),
+        ("dout", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("do_stride", ctypes.c_int64 * 4),
+        ("dq_stride", ctypes.c_int64 * 4),
+        ("dk_stride", ctypes.c_int64 * 4),
+        ("dv_stride", ctypes.c_int64 * 4),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
         ("rsv", ctypes.c_uint8 * 16),
     ]
 
@@ -191,6 +214,11 @@ def lib() -> ctypes.CDLL:
     L.rope_decode_workspace_size.argtypes = [ctypes.POINTER(RopeDecodeParams)]
     L.rope_decode_workspace_size.restype = ctypes.c_uint64
     L.rope_decode_params_size.restype = ctypes.c_uint32
+    L.rope_flash_attn_bwd.argtypes = [ctypes.POINTER(RopeAttnBwdParams), vp]
+    L.rope_flash_attn_bwd.restype = st
+    L.rope_flash_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(RopeAttnBwdParams)]
+    L.rope_flash_attn_bwd_workspace_size.restype = ctypes.c_uint64
+    L.rope_attn_bwd_params_size.restype = ctypes.c_uint32
     L.rope_status_str.argtypes = [ctypes.c_int]
     L.rope_status_str.restype = ctypes.c_char_p
     L.rope_abi_version.restype = i32
@@ -203,6 +231,8 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError("rope_kv_cache_params layout mismatch between binding and library")
     if L.rope_decode_params_size() != ctypes.sizeof(RopeDecodeParams):
         raise RuntimeError("rope_decode_params layout mismatch between binding and library")
+    if L.rope_attn_bwd_params_size() != ctypes.sizeof(RopeAttnBwdParams):
+        raise RuntimeError("rope_attn_bwd_params layout mismatch between binding and library")
     _lib = L
     return L
 
@@ -411,6 +441,50 @@ def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: 
         p.lse = lse.data_ptr()
     _check("rope_flash_attn_fwd", lib().rope_flash_attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------------------- rope_flash_attn_bwd
+def rope_flash_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                        dout: torch.Tensor, cos: Optional[torch.Tensor] = None, sin: Optional[torch.Tensor] = None, *,
+                        causal: bool = True, softmax_scale: Optional[float] = None, layout: str = "BNSD",
+                        cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                        table_seq_rows: int = 0, pairing: str = "half", dq: Optional[torch.Tensor] = None,
+                        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """(dq, dk, dv) for the forward call with the same arguments, given its out and lse."""
+    _need_cuda(q, k, v, out, lse, dout, cos, sin, cu_seqlens, dq, dk, dv, workspace)
+    f = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    f.pairing = PAIRING[pairing]
+    if v.shape != k.shape or v.dtype != q.dtype or out.shape != q.shape or dout.shape != q.shape \
+            or dout.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("v must match k; out and dout must match q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != f.hq * f.ntokens:
+        raise ValueError("lse must be the forward's contiguous float32 [hq, ntokens]")
+    f.v, f.out, f.lse = v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    f.v_stride[:] = _strides(v, layout)
+    f.o_stride[:] = _strides(out, layout)
+    f.causal = 1 if causal else 0
+    f.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / q.shape[-1] ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g, x in ((dq, q), (dk, k), (dv, v)):
+        if g.shape != x.shape or g.dtype != x.dtype:
+            raise ValueError("gradients must match their inputs")
+    p = RopeAttnBwdParams()
+    p.struct_size = ctypes.sizeof(RopeAttnBwdParams)
+    p.fwd = f
+    p.dout, p.dq, p.dk, p.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    p.do_stride[:] = _strides(dout, layout)
+    p.dq_stride[:] = _strides(dq, layout)
+    p.dk_stride[:] = _strides(dk, layout)
+    p.dv_stride[:] = _strides(dv, layout)
+    need = int(lib().rope_flash_attn_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check("rope_flash_attn_bwd", lib().rope_flash_attn_bwd(ctypes.byref(p), _stream(q)))
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------- rope_kv_rms_norm_rope_cache

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librope_fa.so")
 SOURCES = ["api.cpp", "rope_tables.hip", "rope_qk.hip", "flash_fwd.hip", "flash_fwd_bf16.hip", "flash_fwd_f16.hip",
-           "kv_cache.hip", "decode.hip"]
+           "kv_cache.hip", "decode.hip", "flash_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

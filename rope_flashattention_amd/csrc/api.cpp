@@ -22,6 +22,8 @@ hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
 hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream);
 hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream);
+hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream);
+uint64_t flash_bwd_workspace_bytes(const rope_attn_params* f);
 int decode_num_splits(const rope_decode_params* p);
 uint64_t decode_workspace_bytes(const rope_decode_params* p, int nsplit);
 }  // namespace ropefa
@@ -157,6 +159,31 @@ rope_status check_kv_cache(const rope_kv_cache_params* p) {
     return ROPE_OK;
 }
 
+// Checks of rope_attn_bwd_params up to (not including) the workspace.
+rope_status check_bwd_shape(const rope_attn_bwd_params* p) {
+    if (!p) return ROPE_ERR_NULL;
+    if (p->struct_size != sizeof(rope_attn_bwd_params)) return ROPE_ERR_ABI;
+    for (unsigned char c : p->rsv)
+        if (c) return ROPE_ERR_ABI;
+    const rope_attn_params* f = &p->fwd;
+    rope_status st = check_params(f, true);
+    if (st != ROPE_OK) return st;
+    if (f->dtype == ROPE_DT_F32) return ROPE_ERR_UNSUPPORTED;
+    if (!f->cos && f->pos) return ROPE_ERR_UNSUPPORTED;   // tables formed in the kernel: forward only
+    if (!f->lse) return ROPE_ERR_NULL;
+    if (!p->dout || !p->dq || !p->dk || !p->dv) return ROPE_ERR_NULL;
+    const bool varlen = f->cu_seqlens != nullptr;
+    const int eb = dtype_bytes(f->dtype);
+    if ((st = check_strides(p->do_stride, eb, varlen)) != ROPE_OK) return st;
+    if ((st = check_strides(p->dq_stride, eb, varlen)) != ROPE_OK) return st;
+    if ((st = check_strides(p->dk_stride, eb, varlen)) != ROPE_OK) return st;
+    if ((st = check_strides(p->dv_stride, eb, varlen)) != ROPE_OK) return st;
+    if (!aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv))
+        return ROPE_ERR_UNSUPPORTED;
+    if (f->hq > 65535) return ROPE_ERR_LIMIT;   // grid dimension of the dq kernel
+    return ROPE_OK;
+}
+
 // Shape checks of rope_decode_params that the workspace size depends on.
 rope_status check_decode_shape(const rope_decode_params* p) {
     if (!p) return ROPE_ERR_NULL;
@@ -237,6 +264,13 @@ uint32_t rope_attn_params_size(void) { return (uint32_t)sizeof(rope_attn_params)
 uint32_t rope_kv_cache_params_size(void) { return (uint32_t)sizeof(rope_kv_cache_params); }
 
 uint32_t rope_decode_params_size(void) { return (uint32_t)sizeof(rope_decode_params); }
+
+uint32_t rope_attn_bwd_params_size(void) { return (uint32_t)sizeof(rope_attn_bwd_params); }
+
+uint64_t rope_flash_attn_bwd_workspace_size(const rope_attn_bwd_params* p) {
+    if (check_bwd_shape(p) != ROPE_OK) return 0;
+    return ropefa::flash_bwd_workspace_bytes(&p->fwd);
+}
 
 uint64_t rope_decode_workspace_size(const rope_decode_params* p) {
     if (check_decode_shape(p) != ROPE_OK) return 0;
@@ -324,6 +358,16 @@ rope_status rope_decode_attn_fwd(const rope_decode_params* p, void* hip_stream) 
     const rope_status st = check_decode(p);
     if (st != ROPE_OK) return st;
     const hipError_t e = ropefa::launch_decode(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_flash_attn_bwd(const rope_attn_bwd_params* p, void* hip_stream) {
+    const rope_status st = check_bwd_shape(p);
+    if (st != ROPE_OK) return st;
+    const uint64_t need = ropefa::flash_bwd_workspace_bytes(&p->fwd);
+    if (!p->workspace || (reinterpret_cast<uintptr_t>(p->workspace) & 255u) || p->workspace_bytes < need)
+        return ROPE_ERR_WORKSPACE;
+    const hipError_t e = ropefa::launch_flash_bwd(p, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 

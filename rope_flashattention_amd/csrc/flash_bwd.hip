@@ -1,0 +1,617 @@
+// rope_flash_attn_bwd: gradients of RoPE fused into FlashAttention, on gfx950.
+//
+// What is computed (the derivatives of the forward definition; the [FlashAttention blog]
+// says the operator serves training): per (sequence, q head) with q' = M q and k' = M k the
+// rotated rows (M the token's Rope-op matrix), S = s * q'k'^T, P = softmax(S) recomputed
+// from the forward's lse, and dO the output gradient,
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta = rowsum(dO * O),
+//   dq' = s * dS k',  dk' = s * dS^T q',  dq = M^T dq',  dk = M^T dk'.
+// GQA: a kv head's dk and dv sum over the q heads of its group.
+//
+// Three kernels, no atomics:
+//   * bwd_delta_kernel: delta per (query row, q head) into the workspace.
+//   * bwd_dkv_kernel: a workgroup of 4 waves owns 128 keys of one (sequence, kv head); each
+//     wave keeps its 32 keys' rotated K' and V as MFMA B operands in registers and
+//     accumulates dV^T and dK'^T over every q head of the group and every query block of
+//     32 rows that can see its keys.  Per block: S and dP with the 32x32x16 MFMA (A = the
+//     block's Q' and dO rows read from LDS in the permuted row order pi, which leaves each
+//     lane half with 16 consecutive queries of one key), then dV^T += dO^T P and
+//     dK'^T += Q'^T dS with the transposing LDS read (ds_read_b64_tr_b16) supplying
+//     dO^T and Q'^T.
+//   * bwd_dq_kernel: a workgroup of 4 waves owns 128 query rows of one (sequence, q head);
+//     each wave keeps its 32 rows' Q' and dO as B operands and, per 64-key tile staged in
+//     LDS (K' rotated while staging, V), forms S^T, dP^T and dS^T and accumulates
+//     dQ'^T += K'^T dS^T (K'^T by the transposing read).
+// Each LDS tile read both ways is stored twice with different 16-byte chunk XOR swizzles
+// (row reads: pi-row groups, transposing reads: 4-row groups), both bank-conflict free.
+// The epilogues apply M^T (the transposed Rope op) to dq' and dk' before the stores.
+#include "common.h"
+
+namespace ropefa {
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    const void* cos;
+    const void* sin;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;                // workspace [hq, lse_stride]
+    const int32_t* cu_seqlens;   // nullptr: dense
+    int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // {batch, token, head}
+    int32_t batch, hq, hkv, group, seqlen, table_seq_rows, lse_stride, causal;
+    int32_t rows;                // query rows in total (dense batch*seqlen, varlen ntokens)
+    float scale, scale_log2;
+};
+
+template <typename T> struct BMma;
+template <> struct BMma<__bf16> {
+    __device__ static __forceinline__ f32x16 run(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+template <> struct BMma<_Float16> {
+    __device__ static __forceinline__ f32x16 run(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ i16x4 bwd_tr16(const void* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+// MFMA row m holds row pi(m) of a 32-row block: lane half h then holds rows 16h .. 16h+15
+__device__ __forceinline__ int pi_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+// chunk swizzles: for the row reads (8 lanes = rows {0..3, 16..19} + 4k) and for the
+// transposing reads (4 consecutive rows x 2 chunks per 16 lanes)
+__device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 4) & 1) << 2); }
+__device__ __forceinline__ int swz_tr(int r) { return 2 * (r & 3); }
+
+struct BwdSeq {
+    int L;
+    int64_t tok;     // lse / delta index of row 0
+    int64_t tab;     // table row of row 0
+    int64_t bq, bk, bv, bo, bdo, bdq, bdk, bdv;
+};
+__device__ __forceinline__ BwdSeq bwd_seq(const BwdArgs& a, int b) {
+    BwdSeq s;
+    if (a.cu_seqlens) {
+        const int s0 = a.cu_seqlens[b];
+        s.L = a.cu_seqlens[b + 1] - s0;
+        s.tok = s0;
+        s.tab = s0;
+        s.bq = (int64_t)s0 * a.qs[1];
+        s.bk = (int64_t)s0 * a.ks[1];
+        s.bv = (int64_t)s0 * a.vs[1];
+        s.bo = (int64_t)s0 * a.os[1];
+        s.bdo = (int64_t)s0 * a.dos[1];
+        s.bdq = (int64_t)s0 * a.dqs[1];
+        s.bdk = (int64_t)s0 * a.dks[1];
+        s.bdv = (int64_t)s0 * a.dvs[1];
+    } else {
+        s.L = a.seqlen;
+        s.tok = (int64_t)b * a.seqlen;
+        s.tab = a.table_seq_rows ? (int64_t)b * a.table_seq_rows : 0;
+        s.bq = (int64_t)b * a.qs[0];
+        s.bk = (int64_t)b * a.ks[0];
+        s.bv = (int64_t)b * a.vs[0];
+        s.bo = (int64_t)b * a.os[0];
+        s.bdo = (int64_t)b * a.dos[0];
+        s.bdq = (int64_t)b * a.dqs[0];
+        s.bdk = (int64_t)b * a.dks[0];
+        s.bdv = (int64_t)b * a.dvs[0];
+    }
+    return s;
+}
+
+// The Rope op (M) on a chunk pair: x = columns d..d+7, y = columns d+D/2..d+D/2+7 of one row.
+template <typename T, int PAIR>
+__device__ __forceinline__ void rope_fwd_pair(float (&x)[8], float (&y)[8], const T* crow, const T* srow, int d,
+                                              int half) {
+    if (PAIR == 0) return;
+    float c0[8], s0[8], c1[8], s1[8];
+    unpack<T>(load_chunk<T>(crow + d), c0);
+    unpack<T>(load_chunk<T>(srow + d), s0);
+    unpack<T>(load_chunk<T>(crow + d + half), c1);
+    unpack<T>(load_chunk<T>(srow + d + half), s1);
+    if (PAIR == 1) {
+        rotate_pair(x, y, c0, s0, c1, s1);
+    } else {
+        rotate_interleaved(x, c0, s0);
+        rotate_interleaved(y, c1, s1);
+    }
+}
+
+// ============================================================================ delta
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+    constexpr int CH = D / 8;  // lanes per (row, head), a power of two
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t idx = gid / CH;
+    const int c = (int)(gid - idx * CH);
+    const int64_t row = idx / a.hq;
+    const int h = (int)(idx - row * a.hq);
+    if (row >= a.rows) return;  // the whole CH-lane group leaves together
+    int64_t oo, od;
+    if (a.cu_seqlens) {
+        oo = row * a.os[1];
+        od = row * a.dos[1];
+    } else {
+        const int64_t b = row / a.seqlen, s = row - b * a.seqlen;
+        oo = b * a.os[0] + s * a.os[1];
+        od = b * a.dos[0] + s * a.dos[1];
+    }
+    float x[8], y[8];
+    unpack<T>(load_chunk<T>(reinterpret_cast<const T*>(a.o) + oo + (int64_t)h * a.os[2] + c * 8), x);
+    unpack<T>(load_chunk<T>(reinterpret_cast<const T*>(a.dout) + od + (int64_t)h * a.dos[2] + c * 8), y);
+    float sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum = __builtin_fmaf(x[e], y[e], sum);
+#pragma unroll
+    for (int m = CH >> 1; m > 0; m >>= 1) sum += __shfl_xor(sum, m, CH);
+    if (c == 0) a.delta[(int64_t)h * a.lse_stride + row] = sum;
+}
+
+// Epilogue helper: scale the 4-value groups of a transposed accumulator (lane holds column
+// n; rows d = mb*32 + 8*q4 + 4*hh + e), apply M^T with the table row, and store the row.
+template <typename T, int D, int PAIR>
+__device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], float scale, int hh, const T* crow,
+                                               const T* srow, T* dst) {
+    constexpr int HALF = D / 2;
+    float g[D / 32][16];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) g[mb][i] = acc[mb][i] * scale;
+    if (PAIR == 1) {
+        // M^T for pairs (j, j + D/2): g'_j = c_j g_j + s_{j+D/2} g_{j+D/2}, g'_{j+D/2} = c_{j+D/2} g_{j+D/2} - s_j g_j
+#pragma unroll
+        for (int mb = 0; mb < D / 64; ++mb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = mb * 32 + 8 * q4 + 4 * hh;
+                float c0[4], s0[4], c1[4], s1[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    c0[e] = (float)crow[d0 + e];
+                    s0[e] = (float)srow[d0 + e];
+                    c1[e] = (float)crow[d0 + HALF + e];
+                    s1[e] = (float)srow[d0 + HALF + e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = g[mb][4 * q4 + e], y = g[mb + D / 64][4 * q4 + e];
+                    g[mb][4 * q4 + e] = __builtin_fmaf(x, c0[e], __fmul_rn(y, s1[e]));
+                    g[mb + D / 64][4 * q4 + e] = __builtin_fmaf(y, c1[e], -__fmul_rn(x, s0[e]));
+                }
+            }
+    } else if (PAIR == 2) {
+        // M^T for pairs (2k, 2k+1): g'_2k = c_2k g_2k + s_2k+1 g_2k+1, g'_2k+1 = c_2k+1 g_2k+1 - s_2k g_2k
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = mb * 32 + 8 * q4 + 4 * hh;
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const float c0 = (float)crow[d0 + e], s0 = (float)srow[d0 + e];
+                    const float c1 = (float)crow[d0 + e + 1], s1 = (float)srow[d0 + e + 1];
+                    const float x = g[mb][4 * q4 + e], y = g[mb][4 * q4 + e + 1];
+                    g[mb][4 * q4 + e] = __builtin_fmaf(x, c0, __fmul_rn(y, s1));
+                    g[mb][4 * q4 + e + 1] = __builtin_fmaf(y, c1, -__fmul_rn(x, s0));
+                }
+            }
+    }
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = mb * 32 + 8 * q4 + 4 * hh;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<u32x2*>(dst + d0) = u32x2{Elem<T>::pack(g[mb][4 * q4], g[mb][4 * q4 + 1]),
+                                                            Elem<T>::pack(g[mb][4 * q4 + 2], g[mb][4 * q4 + 3])};
+            }
+        }
+}
+
+// ============================================================================ dk, dv
+template <typename T, int D, int PAIR>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+    constexpr int NS = D / 16;
+    constexpr int HALF = D / 2;
+    constexpr int QITEMS = 32 * (D / 16);  // (row, chunk pair) staging items of a 32-row block
+    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) T sQa[32 * D];
+    __shared__ __attribute__((aligned(16))) T sQt[32 * D];
+    __shared__ __attribute__((aligned(16))) T sDa[32 * D];
+    __shared__ __attribute__((aligned(16))) T sDt[32 * D];
+    __shared__ __attribute__((aligned(16))) float sL[32];
+    __shared__ __attribute__((aligned(16))) float sDel[32];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const BwdSeq sq = bwd_seq(a, b);
+    const int L = sq.L;
+    const int k0 = blockIdx.x * 128;
+    if (k0 >= L) return;  // whole workgroup
+    const int kw0 = k0 + 32 * w;
+    const bool active = kw0 < L;
+    const int key = min(kw0 + n, L - 1);
+
+    const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
+    const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
+
+    // ---- this lane's key: rotated K' and V as B operands (column n = key, k = d)
+    u32x4 kb[NS], vb[NS];
+    {
+        const T* kp = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)key * a.ks[1] + (int64_t)kvh * a.ks[2];
+        const T* vp = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)key * a.vs[1] + (int64_t)kvh * a.vs[2];
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int d = 16 * s + 8 * hh;
+            float x[8], y[8];
+            unpack<T>(load_chunk<T>(kp + d), x);
+            unpack<T>(load_chunk<T>(kp + d + HALF), y);
+            rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)key * D, Sg + (int64_t)key * D, d, HALF);
+            kb[s] = pack<T>(x).w;
+            kb[s + NS / 2] = pack<T>(y).w;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
+    }
+
+    f32x16 dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dvacc[mb][i] = dkacc[mb][i] = 0.0f;
+    const int tr_row = (l & 15) >> 2;
+    const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
+    const int pr = pi_row(n), fr = swz_row(pr);
+    const int q_begin = a.causal ? k0 : 0;
+
+    for (int hi = 0; hi < a.group; ++hi) {
+        const int h = kvh * a.group + hi;
+        const T* Qg = reinterpret_cast<const T*>(a.q) + sq.bq + (int64_t)h * a.qs[2];
+        const T* Dg = reinterpret_cast<const T*>(a.dout) + sq.bdo + (int64_t)h * a.dos[2];
+        for (int q0 = q_begin; q0 < L; q0 += 32) {
+            __syncthreads();  // the previous block's LDS reads are done
+            // ---- stage the block's Q' (rotated) and dO rows, twice each (two swizzles)
+            if (tid < QITEMS) {
+                const int r = tid / (D / 16), c = (tid % (D / 16)) * 8;
+                const int qi = q0 + r;
+                float x[8] = {}, y[8] = {}, dx[8] = {}, dy[8] = {};
+                if (qi < L) {
+                    const T* qp = Qg + (int64_t)qi * a.qs[1];
+                    unpack<T>(load_chunk<T>(qp + c), x);
+                    unpack<T>(load_chunk<T>(qp + c + HALF), y);
+                    rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)qi * D, Sg + (int64_t)qi * D, c, HALF);
+                    const T* dp = Dg + (int64_t)qi * a.dos[1];
+                    unpack<T>(load_chunk<T>(dp + c), dx);
+                    unpack<T>(load_chunk<T>(dp + c + HALF), dy);
+                }
+                const int c0 = c / 8, c1 = (c + HALF) / 8;
+                const u32x4 px = pack<T>(x).w, py = pack<T>(y).w, pdx = pack<T>(dx).w, pdy = pack<T>(dy).w;
+                *reinterpret_cast<u32x4*>(&sQa[r * D + 8 * (c0 ^ swz_row(r))]) = px;
+                *reinterpret_cast<u32x4*>(&sQa[r * D + 8 * (c1 ^ swz_row(r))]) = py;
+                *reinterpret_cast<u32x4*>(&sQt[r * D + 8 * (c0 ^ swz_tr(r))]) = px;
+                *reinterpret_cast<u32x4*>(&sQt[r * D + 8 * (c1 ^ swz_tr(r))]) = py;
+                *reinterpret_cast<u32x4*>(&sDa[r * D + 8 * (c0 ^ swz_row(r))]) = pdx;
+                *reinterpret_cast<u32x4*>(&sDa[r * D + 8 * (c1 ^ swz_row(r))]) = pdy;
+                *reinterpret_cast<u32x4*>(&sDt[r * D + 8 * (c0 ^ swz_tr(r))]) = pdx;
+                *reinterpret_cast<u32x4*>(&sDt[r * D + 8 * (c1 ^ swz_tr(r))]) = pdy;
+            }
+            if (tid < 32) {
+                const int qi = q0 + tid;
+                const bool ok = qi < L;
+                // rows past the end get lse = +inf: their P is exactly 0
+                sL[tid] = ok ? a.lse[(int64_t)h * a.lse_stride + sq.tok + qi] * kLog2e : __builtin_inff();
+                sDel[tid] = ok ? a.delta[(int64_t)h * a.lse_stride + sq.tok + qi] : 0.0f;
+            }
+            __syncthreads();
+            if (!active || (a.causal && q0 + 31 < kw0)) continue;  // wave-uniform
+
+            // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i
+            f32x16 sacc, dpacc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int off = pr * D + 8 * ((2 * s + hh) ^ fr);
+                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sQa[off]), kb[s], sacc);
+                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sDa[off]), vb[s], dpacc);
+            }
+            float lv[16], dv[16];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[16 * hh + 4 * i4]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[16 * hh + 4 * i4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lv[4 * i4 + e] = l4[e];
+                    dv[4 * i4 + e] = d4[e];
+                }
+            }
+            const int mykey = kw0 + n;
+            u32x4 pk[2], dsk[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float p[8], ds[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = 8 * s + j;
+                    const int qi = q0 + 16 * hh + i;
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv[i]));
+                    if ((a.causal && mykey > qi) || mykey >= L) pv = 0.0f;
+                    p[j] = pv;
+                    ds[j] = pv * (dpacc[i] - dv[i]);
+                }
+                pk[s] = pack<T>(p).w;
+                dsk[s] = pack<T>(ds).w;
+            }
+            // ---- dV^T += dO^T P,  dK'^T += Q'^T dS
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int r = 16 * hh + 8 * s + tr_row;  // r % 4 == tr_row
+                    const int e = mb * 32 + tr_col;
+                    const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
+                    const i16x4 dlo = bwd_tr16(&sDt[r * D + sw]);
+                    const i16x4 dhi = bwd_tr16(&sDt[(r + 4) * D + sw]);
+                    dvacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4,
+                                                                                                5, 6, 7)),
+                                             pk[s], dvacc[mb]);
+                    const i16x4 qlo = bwd_tr16(&sQt[r * D + sw]);
+                    const i16x4 qhi = bwd_tr16(&sQt[(r + 4) * D + sw]);
+                    dkacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4,
+                                                                                                5, 6, 7)),
+                                             dsk[s], dkacc[mb]);
+                }
+        }
+    }
+
+    // ---- epilogue: dk = M^T (s * dK'), dv as accumulated
+    if (active && kw0 + n < L) {
+        const int kr = kw0 + n;
+        T* dkp = reinterpret_cast<T*>(a.dk) + sq.bdk + (int64_t)kr * a.dks[1] + (int64_t)kvh * a.dks[2];
+        T* dvp = reinterpret_cast<T*>(a.dv) + sq.bdv + (int64_t)kr * a.dvs[1] + (int64_t)kvh * a.dvs[2];
+        store_grad_row<T, D, PAIR>(dkacc, a.scale, hh, Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, dkp);
+        store_grad_row<T, D, 0>(dvacc, 1.0f, hh, nullptr, nullptr, dvp);
+    }
+}
+
+// ============================================================================ dq
+template <typename T, int D, int PAIR>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int NS = D / 16;
+    constexpr int HALF = D / 2;
+    constexpr int KITEMS = 64 * (D / 16);  // (key row, chunk pair) staging items of a 64-key tile
+    constexpr int NKI = (KITEMS + 255) / 256;
+    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) T sKa[64 * D];
+    __shared__ __attribute__((aligned(16))) T sKt[64 * D];
+    __shared__ __attribute__((aligned(16))) T sVa[64 * D];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
+    const int qt = gridDim.x - 1 - blockIdx.x;  // longest query tiles first
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int kvh = h / a.group;
+    const BwdSeq sq = bwd_seq(a, b);
+    const int L = sq.L;
+    const int q0 = qt * 128;
+    if (q0 >= L) return;  // whole workgroup
+    const int qw0 = q0 + 32 * w;
+    const bool active = qw0 < L;
+    const int qi = qw0 + n;
+    const int qrow = min(qi, L - 1);
+
+    const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
+    const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
+    const T* Kg = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)kvh * a.ks[2];
+    const T* Vg = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)kvh * a.vs[2];
+
+    // ---- this lane's query row: rotated Q' and dO as B operands (column n = query, k = d)
+    u32x4 qb[NS], db[NS];
+    {
+        const T* qp = reinterpret_cast<const T*>(a.q) + sq.bq + (int64_t)qrow * a.qs[1] + (int64_t)h * a.qs[2];
+        const T* dp = reinterpret_cast<const T*>(a.dout) + sq.bdo + (int64_t)qrow * a.dos[1] + (int64_t)h * a.dos[2];
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int d = 16 * s + 8 * hh;
+            float x[8], y[8];
+            unpack<T>(load_chunk<T>(qp + d), x);
+            unpack<T>(load_chunk<T>(qp + d + HALF), y);
+            rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)qrow * D, Sg + (int64_t)qrow * D, d, HALF);
+            qb[s] = pack<T>(x).w;
+            qb[s + NS / 2] = pack<T>(y).w;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) db[s] = load_chunk<T>(dp + 16 * s + 8 * hh).w;
+    }
+    const float lse2 = a.lse[(int64_t)h * a.lse_stride + sq.tok + qrow] * kLog2e;
+    const float del = a.delta[(int64_t)h * a.lse_stride + sq.tok + qrow];
+
+    f32x16 dqacc[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dqacc[mb][i] = 0.0f;
+    const int tr_row = (l & 15) >> 2;
+    const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
+    const int pr = pi_row(n), fr = swz_row(pr);
+    const int q_hi = min(q0 + 128, L);
+    const int kend = a.causal ? q_hi : L;
+    const int n_kt = (kend + 63) / 64;
+    const int wave_kend = a.causal ? min(qw0 + 32, L) : L;
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * 64;
+        __syncthreads();  // the previous tile's LDS reads are done
+        // ---- stage K' (rotated; row and transposing copies) and V rows; rows past the end
+        // re-read the last row (finite, masked below)
+#pragma unroll
+        for (int j = 0; j < NKI; ++j) {
+            const int it = tid + j * 256;
+            if (KITEMS % 256 == 0 || it < KITEMS) {
+                const int r = it / (D / 16), c = (it % (D / 16)) * 8;
+                const int kr = min(k0 + r, L - 1);
+                const T* kp = Kg + (int64_t)kr * a.ks[1];
+                const T* vp = Vg + (int64_t)kr * a.vs[1];
+                float x[8], y[8];
+                unpack<T>(load_chunk<T>(kp + c), x);
+                unpack<T>(load_chunk<T>(kp + c + HALF), y);
+                rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, c, HALF);
+                const u32x4 v0 = load_chunk<T>(vp + c).w, v1 = load_chunk<T>(vp + c + HALF).w;
+                const int c0 = c / 8, c1 = (c + HALF) / 8;
+                const u32x4 px = pack<T>(x).w, py = pack<T>(y).w;
+                *reinterpret_cast<u32x4*>(&sKa[r * D + 8 * (c0 ^ swz_row(r))]) = px;
+                *reinterpret_cast<u32x4*>(&sKa[r * D + 8 * (c1 ^ swz_row(r))]) = py;
+                *reinterpret_cast<u32x4*>(&sKt[r * D + 8 * (c0 ^ swz_tr(r))]) = px;
+                *reinterpret_cast<u32x4*>(&sKt[r * D + 8 * (c1 ^ swz_tr(r))]) = py;
+                *reinterpret_cast<u32x4*>(&sVa[r * D + 8 * (c0 ^ swz_row(r))]) = v0;
+                *reinterpret_cast<u32x4*>(&sVa[r * D + 8 * (c1 ^ swz_row(r))]) = v1;
+            }
+        }
+        __syncthreads();
+        if (!active || k0 >= wave_kend) continue;  // wave-uniform
+
+        u32x4 dsk[2][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            // ---- S^T and dP^T: lane (n, hh) gets query qi against keys k0 + 32*blk + 16hh + i
+            const int rr = blk * 32 + pr;
+            f32x16 sacc, dpacc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int off = rr * D + 8 * ((2 * s + hh) ^ fr);
+                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sKa[off]), qb[s], sacc);
+                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sVa[off]), db[s], dpacc);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float ds[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = 8 * s + j;
+                    const int kk = k0 + 32 * blk + 16 * hh + i;
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lse2));
+                    if ((a.causal && kk > qi) || kk >= L) pv = 0.0f;
+                    ds[j] = pv * (dpacc[i] - del);
+                }
+                dsk[blk][s] = pack<T>(ds).w;
+            }
+        }
+        // ---- dQ'^T += K'^T dS^T
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
+                    const int e = mb * 32 + tr_col;
+                    const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
+                    const i16x4 lo = bwd_tr16(&sKt[r * D + sw]);
+                    const i16x4 hi = bwd_tr16(&sKt[(r + 4) * D + sw]);
+                    dqacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
+                                                                                                6, 7)),
+                                             dsk[blk][s], dqacc[mb]);
+                }
+    }
+
+    // ---- epilogue: dq = M^T (s * dQ')
+    if (active && qi < L) {
+        T* dqp = reinterpret_cast<T*>(a.dq) + sq.bdq + (int64_t)qi * a.dqs[1] + (int64_t)h * a.dqs[2];
+        store_grad_row<T, D, PAIR>(dqacc, a.scale, hh, Cg + (int64_t)qi * D, Sg + (int64_t)qi * D, dqp);
+    }
+}
+
+// ============================================================================ launch
+template <typename T, int D, int PAIR>
+static void launch_bwd_typed(const BwdArgs& a, int maxlen, hipStream_t stream) {
+    const int64_t dthreads = (int64_t)a.rows * a.hq * (D / 8);
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream, a);
+    const unsigned tiles = (unsigned)((maxlen + 127) / 128);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3(tiles, a.hkv, a.batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR>), dim3(tiles, a.hq, a.batch), dim3(256), 0, stream, a);
+}
+
+template <typename T, int D>
+static void launch_bwd_pair(const BwdArgs& a, int pair, int maxlen, hipStream_t stream) {
+    switch (pair) {
+        case 0: launch_bwd_typed<T, D, 0>(a, maxlen, stream); break;
+        case 1: launch_bwd_typed<T, D, 1>(a, maxlen, stream); break;
+        default: launch_bwd_typed<T, D, 2>(a, maxlen, stream); break;
+    }
+}
+
+uint64_t flash_bwd_workspace_bytes(const rope_attn_params* f) {
+    const int64_t rows = f->cu_seqlens ? (int64_t)f->ntokens : (int64_t)f->batch * f->seqlen;
+    return (uint64_t)rows * (uint64_t)f->hq * 4u;
+}
+
+hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream) {
+    const rope_attn_params* f = &p->fwd;
+    BwdArgs a;
+    a.q = f->q;
+    a.k = f->k;
+    a.v = f->v;
+    a.o = f->out;
+    a.dout = p->dout;
+    a.lse = f->lse;
+    a.cos = f->cos;
+    a.sin = f->sin;
+    a.dq = p->dq;
+    a.dk = p->dk;
+    a.dv = p->dv;
+    a.delta = reinterpret_cast<float*>(p->workspace);
+    a.cu_seqlens = f->cu_seqlens;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = f->q_stride[i];
+        a.ks[i] = f->k_stride[i];
+        a.vs[i] = f->v_stride[i];
+        a.os[i] = f->o_stride[i];
+        a.dos[i] = p->do_stride[i];
+        a.dqs[i] = p->dq_stride[i];
+        a.dks[i] = p->dk_stride[i];
+        a.dvs[i] = p->dv_stride[i];
+    }
+    const bool varlen = f->cu_seqlens != nullptr;
+    a.batch = f->batch;
+    a.hq = f->hq;
+    a.hkv = f->hkv;
+    a.group = f->hq / f->hkv;
+    a.seqlen = varlen ? 0 : f->seqlen;
+    a.table_seq_rows = f->table_seq_rows;
+    a.rows = varlen ? f->ntokens : f->batch * f->seqlen;
+    a.lse_stride = a.rows;
+    a.causal = f->causal;
+    a.scale = f->softmax_scale;
+    a.scale_log2 = f->softmax_scale * 1.4426950408889634f;
+    const int pair = f->cos ? (f->pairing == ROPE_PAIR_INTERLEAVED ? 2 : 1) : 0;
+    const int maxlen = varlen ? f->max_seqlen : f->seqlen;
+    const int key = (f->dtype == ROPE_DT_BF16 ? 0 : 2) + (f->head_dim == 128 ? 1 : 0);
+    switch (key) {
+        case 0: launch_bwd_pair<__bf16, 64>(a, pair, maxlen, stream); break;
+        case 1: launch_bwd_pair<__bf16, 128>(a, pair, maxlen, stream); break;
+        case 2: launch_bwd_pair<_Float16, 64>(a, pair, maxlen, stream); break;
+        default: launch_bwd_pair<_Float16, 128>(a, pair, maxlen, stream); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ropefa

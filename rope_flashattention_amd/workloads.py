@@ -123,6 +123,12 @@ def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
     return Inputs(w, q, k, v, seq_lens, pos)
 
 
+def generate_dout(inp: Inputs, seed: int) -> torch.Tensor:
+    """A seeded output gradient dO ~ N(0, 1), shaped like inp.q, rounded to the workload dtype."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _normal(rng, tuple(inp.q.shape), inp.workload.torch_dtype)
+
+
 def cu_seqlens(seq_lens) -> np.ndarray:
     """[batch + 1] int32 prefix sums starting at 0 (index bookkeeping for packed batches)."""
     return np.concatenate([[0], np.cumsum(np.asarray(seq_lens, dtype=np.int64))]).astype(np.int32)

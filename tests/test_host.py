@@ -15,7 +15,7 @@ import pytest
 
 import oracle as orc
 import rope_flashattention_amd as rfa
-from rope_flashattention_amd import RopeAttnParams, RopeDecodeParams, RopeKvCacheParams
+from rope_flashattention_amd import RopeAttnBwdParams, RopeAttnParams, RopeDecodeParams, RopeKvCacheParams
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rope_fa.h")
@@ -38,7 +38,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(ropelib):
     names = declared_functions()
     assert {"rope_tables", "rope_qk", "rope_flash_attn_fwd", "rope_inv_freq",
-            "rope_kv_rms_norm_rope_cache", "rope_decode_attn_fwd", "rope_decode_workspace_size"} <= set(names)
+            "rope_kv_rms_norm_rope_cache", "rope_decode_attn_fwd", "rope_decode_workspace_size",
+            "rope_flash_attn_bwd", "rope_flash_attn_bwd_workspace_size", "rope_tables_ex"} <= set(names)
     for n in names:
         assert hasattr(ropelib, n), n
 
@@ -48,6 +49,7 @@ def test_abi_version_and_struct_size(ropelib):
     assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
     assert ropelib.rope_kv_cache_params_size() == ctypes.sizeof(RopeKvCacheParams)
     assert ropelib.rope_decode_params_size() == ctypes.sizeof(RopeDecodeParams)
+    assert ropelib.rope_attn_bwd_params_size() == ctypes.sizeof(RopeAttnBwdParams)
     for s, name in rfa.STATUS.items():
         assert ropelib.rope_status_str(s).decode() == name
 
@@ -255,6 +257,66 @@ def test_cache_and_decode_pairing_rejects(ropelib):
     assert ropelib.rope_kv_rms_norm_rope_cache(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
     p = mutate(valid_decode_params(), pairing=5)
     assert ropelib.rope_decode_attn_fwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+
+
+# --------------------------------------------------------------------------- backward validation
+def valid_bwd_params(**fwd_kw):
+    p = RopeAttnBwdParams()
+    p.struct_size = ctypes.sizeof(RopeAttnBwdParams)
+    p.fwd = valid_params(**fwd_kw)
+    p.fwd.lse = FAKE
+    p.dout = p.dq = p.dk = p.dv = FAKE
+    p.do_stride[:] = p.dq_stride[:] = tuple(p.fwd.q_stride)
+    p.dk_stride[:] = p.dv_stride[:] = tuple(p.fwd.k_stride)
+    p.workspace = 0x100000
+    p.workspace_bytes = 1 << 30
+    return p
+
+
+def test_bwd_workspace_size(ropelib):
+    p = valid_bwd_params()
+    # one float per (query row, q head): B2 x S100 rows, 8 heads
+    assert ropelib.rope_flash_attn_bwd_workspace_size(ctypes.byref(p)) == 2 * 100 * 8 * 4
+    p.fwd.lse = None
+    assert ropelib.rope_flash_attn_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), "ROPE_ERR_ABI"),
+    (dict(rsv=1), "ROPE_ERR_ABI"),
+    (dict(dout=None), "ROPE_ERR_NULL"),
+    (dict(dq=None), "ROPE_ERR_NULL"),
+    (dict(dk=None), "ROPE_ERR_NULL"),
+    (dict(dv=None), "ROPE_ERR_NULL"),
+    (dict(dk=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
+    (dict(dq_stride=(8 * 100 * 128, 128, 100 * 128, 2)), "ROPE_ERR_UNSUPPORTED"),
+    (dict(workspace=None), "ROPE_ERR_WORKSPACE"),
+    (dict(workspace=0x100000 + 64), "ROPE_ERR_WORKSPACE"),
+    (dict(workspace_bytes=100), "ROPE_ERR_WORKSPACE"),
+])
+def test_bwd_rejects(ropelib, kw, status):
+    p = mutate(valid_bwd_params(), **kw)
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST[status]
+
+
+@no_gpu_only
+def test_bwd_rejects_forward_fields(ropelib):
+    p = valid_bwd_params()
+    p.fwd.lse = None
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_NULL"]
+    p = valid_bwd_params(dtype=3, D=64)
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+    p = valid_bwd_params()
+    p.fwd.cos = p.fwd.sin = None
+    p.fwd.pos, p.fwd.inv_freq, p.fwd.inv_freq_rows, p.fwd.pos_scale = FAKE, FAKE, 1, 1.0
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+    p = valid_bwd_params()
+    p.fwd.struct_size = 4
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_ABI"]
+    p = valid_bwd_params(D=96)
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+    assert ropelib.rope_flash_attn_bwd(None, None) == ST["ROPE_ERR_NULL"]
 
 
 @no_gpu_only
