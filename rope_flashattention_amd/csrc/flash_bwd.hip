@@ -81,33 +81,33 @@ struct BwdSeq {
     int64_t bq, bk, bv, bo, bdo, bdq, bdk, bdv;
 };
 __device__ __forceinline__ BwdSeq bwd_seq(const BwdArgs& a, int b) {
+    // base offset = ib * stride[0] + it * stride[1] with (ib, it) = (b, 0) dense and
+    // (0, first token) varlen: constant stride indices (a selected index would put the
+    // argument block in scratch memory)
     BwdSeq s;
+    int64_t ib, it;
     if (a.cu_seqlens) {
         const int s0 = a.cu_seqlens[b];
         s.L = a.cu_seqlens[b + 1] - s0;
         s.tok = s0;
         s.tab = s0;
-        s.bq = (int64_t)s0 * a.qs[1];
-        s.bk = (int64_t)s0 * a.ks[1];
-        s.bv = (int64_t)s0 * a.vs[1];
-        s.bo = (int64_t)s0 * a.os[1];
-        s.bdo = (int64_t)s0 * a.dos[1];
-        s.bdq = (int64_t)s0 * a.dqs[1];
-        s.bdk = (int64_t)s0 * a.dks[1];
-        s.bdv = (int64_t)s0 * a.dvs[1];
+        ib = 0;
+        it = s0;
     } else {
         s.L = a.seqlen;
         s.tok = (int64_t)b * a.seqlen;
         s.tab = a.table_seq_rows ? (int64_t)b * a.table_seq_rows : 0;
-        s.bq = (int64_t)b * a.qs[0];
-        s.bk = (int64_t)b * a.ks[0];
-        s.bv = (int64_t)b * a.vs[0];
-        s.bo = (int64_t)b * a.os[0];
-        s.bdo = (int64_t)b * a.dos[0];
-        s.bdq = (int64_t)b * a.dqs[0];
-        s.bdk = (int64_t)b * a.dks[0];
-        s.bdv = (int64_t)b * a.dvs[0];
+        ib = b;
+        it = 0;
     }
+    s.bq = ib * a.qs[0] + it * a.qs[1];
+    s.bk = ib * a.ks[0] + it * a.ks[1];
+    s.bv = ib * a.vs[0] + it * a.vs[1];
+    s.bo = ib * a.os[0] + it * a.os[1];
+    s.bdo = ib * a.dos[0] + it * a.dos[1];
+    s.bdq = ib * a.dqs[0] + it * a.dqs[1];
+    s.bdk = ib * a.dks[0] + it * a.dks[1];
+    s.bdv = ib * a.dvs[0] + it * a.dvs[1];
     return s;
 }
 
@@ -221,19 +221,81 @@ __device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], floa
         }
 }
 
+// ============================================================================ staging
+// One staging item: the 8-element chunks at columns c and c + D/2 of one row of two
+// tensors (the first is rotated, the second copied) and, when rotating, the row's table
+// chunks at the same columns.  Loaded one block ahead into registers, rotated and written
+// to LDS at the start of the next block.
+struct StageItem {
+    u32x4 a0, a1, b0, b1, c0, c1, s0, s1;
+};
+
+template <typename T, int PAIR>
+__device__ __forceinline__ void stage_load(StageItem& s, const T* arow, const T* brow, const T* crow, const T* srow,
+                                           int c, int half) {
+    s.a0 = load_chunk<T>(arow + c).w;
+    s.a1 = load_chunk<T>(arow + c + half).w;
+    s.b0 = load_chunk<T>(brow + c).w;
+    s.b1 = load_chunk<T>(brow + c + half).w;
+    if (PAIR != 0) {
+        s.c0 = load_chunk<T>(crow + c).w;
+        s.c1 = load_chunk<T>(crow + c + half).w;
+        s.s0 = load_chunk<T>(srow + c).w;
+        s.s1 = load_chunk<T>(srow + c + half).w;
+    }
+}
+
+// The Rope op (M) on a staged item's first tensor, rounded once to T.
+template <typename T, int PAIR>
+__device__ __forceinline__ void stage_rotate(const StageItem& s, u32x4& px, u32x4& py) {
+    if (PAIR == 0) {
+        px = s.a0;
+        py = s.a1;
+        return;
+    }
+    float x[8], y[8], c0[8], s0[8], c1[8], s1[8];
+    unpack<T>(Chunk8<T>{s.a0}, x);
+    unpack<T>(Chunk8<T>{s.a1}, y);
+    unpack<T>(Chunk8<T>{s.c0}, c0);
+    unpack<T>(Chunk8<T>{s.s0}, s0);
+    unpack<T>(Chunk8<T>{s.c1}, c1);
+    unpack<T>(Chunk8<T>{s.s1}, s1);
+    if (PAIR == 1) {
+        rotate_pair(x, y, c0, s0, c1, s1);
+    } else {
+        rotate_interleaved(x, c0, s0);
+        rotate_interleaved(y, c1, s1);
+    }
+    px = pack<T>(x).w;
+    py = pack<T>(y).w;
+}
+
+// Writes chunk pair (c/8, (c+D/2)/8) of row r into a row-read copy and a transposing-read
+// copy of an LDS tile (different XOR swizzles).
+template <typename T, int D>
+__device__ __forceinline__ void stage_store2(T* ta, T* tt, int r, int c, const u32x4& x, const u32x4& y) {
+    const int c0 = c / 8, c1 = (c + D / 2) / 8;
+    *reinterpret_cast<u32x4*>(&ta[r * D + 8 * (c0 ^ swz_row(r))]) = x;
+    *reinterpret_cast<u32x4*>(&ta[r * D + 8 * (c1 ^ swz_row(r))]) = y;
+    *reinterpret_cast<u32x4*>(&tt[r * D + 8 * (c0 ^ swz_tr(r))]) = x;
+    *reinterpret_cast<u32x4*>(&tt[r * D + 8 * (c1 ^ swz_tr(r))]) = y;
+}
+
 // ============================================================================ dk, dv
 template <typename T, int D, int PAIR>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int NS = D / 16;
     constexpr int HALF = D / 2;
-    constexpr int QITEMS = 32 * (D / 16);  // (row, chunk pair) staging items of a 32-row block
+    constexpr int CPR = D / 16;        // chunk pairs per row
+    constexpr int QITEMS = 32 * CPR;   // staging items of a 32-row block (<= 256)
     constexpr float kLog2e = 1.4426950408889634f;
-    __shared__ __attribute__((aligned(16))) T sQa[32 * D];
-    __shared__ __attribute__((aligned(16))) T sQt[32 * D];
-    __shared__ __attribute__((aligned(16))) T sDa[32 * D];
-    __shared__ __attribute__((aligned(16))) T sDt[32 * D];
-    __shared__ __attribute__((aligned(16))) float sL[32];
-    __shared__ __attribute__((aligned(16))) float sDel[32];
+    // double-buffered: block i is written to buffer i & 1 while block i - 1 is read
+    __shared__ __attribute__((aligned(16))) T sQa[2][32 * D];
+    __shared__ __attribute__((aligned(16))) T sQt[2][32 * D];
+    __shared__ __attribute__((aligned(16))) T sDa[2][32 * D];
+    __shared__ __attribute__((aligned(16))) T sDt[2][32 * D];
+    __shared__ __attribute__((aligned(16))) float sL[2][32];
+    __shared__ __attribute__((aligned(16))) float sDel[2][32];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
@@ -249,6 +311,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
     const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
+    const T* Qb = reinterpret_cast<const T*>(a.q) + sq.bq;
+    const T* Db = reinterpret_cast<const T*>(a.dout) + sq.bdo;
+
+    // ---- staging role: item (row sr, chunk pair sc) of each 32-row block; rows past the
+    // end re-read the last row (finite values; their P is exactly 0 through lse = +inf)
+    const bool stager = tid < QITEMS;
+    const int sr = (tid % QITEMS) / CPR, sc = (tid % CPR) * 8;
+    // Every thread issues its loads unconditionally (no branch around a load, so no wait
+    // is forced at a join); the loaded values are only used at the next block's store.
+    StageItem pre;
+    float pre_l, pre_d;  // raw lse and delta of row (tid & 31) of the block
+    auto load_block = [&](int hi, int q0) {
+        const int h = kvh * a.group + hi;
+        const int qi = min(q0 + sr, L - 1);
+        stage_load<T, PAIR>(pre, Qb + (int64_t)qi * a.qs[1] + (int64_t)h * a.qs[2],
+                            Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], Cg + (int64_t)qi * D,
+                            Sg + (int64_t)qi * D, sc, HALF);
+        const int64_t idx = (int64_t)h * a.lse_stride + sq.tok + min(q0 + (tid & 31), L - 1);
+        pre_l = a.lse[idx];
+        pre_d = a.delta[idx];
+    };
+    auto store_block = [&](int buf, int q0) {
+        if (stager) {
+            u32x4 px, py;
+            stage_rotate<T, PAIR>(pre, px, py);
+            stage_store2<T, D>(sQa[buf], sQt[buf], sr, sc, px, py);
+            stage_store2<T, D>(sDa[buf], sDt[buf], sr, sc, pre.b0, pre.b1);
+        }
+        if (tid < 32) {
+            // rows past the end get lse = +inf: their P is exactly 0
+            const bool ok = q0 + tid < L;
+            sL[buf][tid] = ok ? pre_l * kLog2e : __builtin_inff();
+            sDel[buf][tid] = ok ? pre_d : 0.0f;
+        }
+    };
 
     // ---- this lane's key: rotated K' and V as B operands (column n = key, k = d)
     u32x4 kb[NS], vb[NS];
@@ -267,6 +364,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
+        // complete these loads here: otherwise the loop's first use would wait for every
+        // load issued after them, the prefetch included
+#pragma unroll
+        for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(vb[s]));
     }
 
     f32x16 dvacc[D / 32], dkacc[D / 32];
@@ -277,49 +378,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
     const int pr = pi_row(n), fr = swz_row(pr);
+    const int mykey = kw0 + n;
+    // P of (query qi, this key) is kept iff qi >= qmin
+    const int qmin = mykey >= L ? (1 << 30) : (a.causal ? mykey : -(1 << 30));
     const int q_begin = a.causal ? k0 : 0;
 
-    for (int hi = 0; hi < a.group; ++hi) {
-        const int h = kvh * a.group + hi;
-        const T* Qg = reinterpret_cast<const T*>(a.q) + sq.bq + (int64_t)h * a.qs[2];
-        const T* Dg = reinterpret_cast<const T*>(a.dout) + sq.bdo + (int64_t)h * a.dos[2];
-        for (int q0 = q_begin; q0 < L; q0 += 32) {
-            __syncthreads();  // the previous block's LDS reads are done
-            // ---- stage the block's Q' (rotated) and dO rows, twice each (two swizzles)
-            if (tid < QITEMS) {
-                const int r = tid / (D / 16), c = (tid % (D / 16)) * 8;
-                const int qi = q0 + r;
-                float x[8] = {}, y[8] = {}, dx[8] = {}, dy[8] = {};
-                if (qi < L) {
-                    const T* qp = Qg + (int64_t)qi * a.qs[1];
-                    unpack<T>(load_chunk<T>(qp + c), x);
-                    unpack<T>(load_chunk<T>(qp + c + HALF), y);
-                    rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)qi * D, Sg + (int64_t)qi * D, c, HALF);
-                    const T* dp = Dg + (int64_t)qi * a.dos[1];
-                    unpack<T>(load_chunk<T>(dp + c), dx);
-                    unpack<T>(load_chunk<T>(dp + c + HALF), dy);
-                }
-                const int c0 = c / 8, c1 = (c + HALF) / 8;
-                const u32x4 px = pack<T>(x).w, py = pack<T>(y).w, pdx = pack<T>(dx).w, pdy = pack<T>(dy).w;
-                *reinterpret_cast<u32x4*>(&sQa[r * D + 8 * (c0 ^ swz_row(r))]) = px;
-                *reinterpret_cast<u32x4*>(&sQa[r * D + 8 * (c1 ^ swz_row(r))]) = py;
-                *reinterpret_cast<u32x4*>(&sQt[r * D + 8 * (c0 ^ swz_tr(r))]) = px;
-                *reinterpret_cast<u32x4*>(&sQt[r * D + 8 * (c1 ^ swz_tr(r))]) = py;
-                *reinterpret_cast<u32x4*>(&sDa[r * D + 8 * (c0 ^ swz_row(r))]) = pdx;
-                *reinterpret_cast<u32x4*>(&sDa[r * D + 8 * (c1 ^ swz_row(r))]) = pdy;
-                *reinterpret_cast<u32x4*>(&sDt[r * D + 8 * (c0 ^ swz_tr(r))]) = pdx;
-                *reinterpret_cast<u32x4*>(&sDt[r * D + 8 * (c1 ^ swz_tr(r))]) = pdy;
-            }
-            if (tid < 32) {
-                const int qi = q0 + tid;
-                const bool ok = qi < L;
-                // rows past the end get lse = +inf: their P is exactly 0
-                sL[tid] = ok ? a.lse[(int64_t)h * a.lse_stride + sq.tok + qi] * kLog2e : __builtin_inff();
-                sDel[tid] = ok ? a.delta[(int64_t)h * a.lse_stride + sq.tok + qi] : 0.0f;
-            }
-            __syncthreads();
-            if (!active || (a.causal && q0 + 31 < kw0)) continue;  // wave-uniform
-
+    // blocks in order (q head of the group, 32-row query block)
+    int ld_hi = 0, ld_q0 = q_begin;
+    load_block(ld_hi, ld_q0);
+    for (int buf = 0;; buf ^= 1) {
+        const int q0 = ld_q0;
+        store_block(buf, q0);
+        __syncthreads();  // block visible; every read of this buffer two blocks back is done
+        ld_q0 += 32;
+        if (ld_q0 >= L) {
+            ld_q0 = q_begin;
+            ++ld_hi;
+        }
+        const bool more = ld_hi < a.group;
+        // after the last block this reloads the first one (never stored): no branch
+        load_block(more ? ld_hi : 0, ld_q0);
+        if (active && !(a.causal && q0 + 31 < kw0)) {  // wave-uniform
+            const T* qa = sQa[buf];
+            const T* qt = sQt[buf];
+            const T* da = sDa[buf];
+            const T* dt = sDt[buf];
             // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i
             f32x16 sacc, dpacc;
 #pragma unroll
@@ -327,21 +410,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int off = pr * D + 8 * ((2 * s + hh) ^ fr);
-                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sQa[off]), kb[s], sacc);
-                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sDa[off]), vb[s], dpacc);
+                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&qa[off]), kb[s], sacc);
+                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&da[off]), vb[s], dpacc);
             }
-            float lv[16], dv[16];
+            const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
+            float lv[16], dl[16];
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[16 * hh + 4 * i4]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[16 * hh + 4 * i4]);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 4 * i4]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 4 * i4]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     lv[4 * i4 + e] = l4[e];
-                    dv[4 * i4 + e] = d4[e];
+                    dl[4 * i4 + e] = d4[e];
                 }
             }
-            const int mykey = kw0 + n;
             u32x4 pk[2], dsk[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -349,11 +432,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int i = 8 * s + j;
-                    const int qi = q0 + 16 * hh + i;
                     float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv[i]));
-                    if ((a.causal && mykey > qi) || mykey >= L) pv = 0.0f;
+                    if (i < thr) pv = 0.0f;
                     p[j] = pv;
-                    ds[j] = pv * (dpacc[i] - dv[i]);
+                    ds[j] = pv * (dpacc[i] - dl[i]);
                 }
                 pk[s] = pack<T>(p).w;
                 dsk[s] = pack<T>(ds).w;
@@ -366,18 +448,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
                     const int r = 16 * hh + 8 * s + tr_row;  // r % 4 == tr_row
                     const int e = mb * 32 + tr_col;
                     const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
-                    const i16x4 dlo = bwd_tr16(&sDt[r * D + sw]);
-                    const i16x4 dhi = bwd_tr16(&sDt[(r + 4) * D + sw]);
+                    const i16x4 dlo = bwd_tr16(&dt[r * D + sw]);
+                    const i16x4 dhi = bwd_tr16(&dt[(r + 4) * D + sw]);
                     dvacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4,
                                                                                                 5, 6, 7)),
                                              pk[s], dvacc[mb]);
-                    const i16x4 qlo = bwd_tr16(&sQt[r * D + sw]);
-                    const i16x4 qhi = bwd_tr16(&sQt[(r + 4) * D + sw]);
+                    const i16x4 qlo = bwd_tr16(&qt[r * D + sw]);
+                    const i16x4 qhi = bwd_tr16(&qt[(r + 4) * D + sw]);
                     dkacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4,
                                                                                                 5, 6, 7)),
                                              dsk[s], dkacc[mb]);
                 }
         }
+        if (!more) break;
     }
 
     // ---- epilogue: dk = M^T (s * dK'), dv as accumulated
@@ -391,16 +474,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ============================================================================ dq
-template <typename T, int D, int PAIR>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+// NW waves of 32 query rows each; key tiles of KT (32 or 64) keys.
+template <typename T, int D, int PAIR, int NW, int KT>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NS = D / 16;
     constexpr int HALF = D / 2;
-    constexpr int KITEMS = 64 * (D / 16);  // (key row, chunk pair) staging items of a 64-key tile
-    constexpr int NKI = (KITEMS + 255) / 256;
+    constexpr int CPR = D / 16;
+    constexpr int NT = NW * 64;
+    constexpr int KITEMS = KT * CPR;  // staging items of a key tile
+    constexpr int NKI = (KITEMS + NT - 1) / NT;
+    constexpr int NB = KT / 32;       // 32-key blocks per tile
     constexpr float kLog2e = 1.4426950408889634f;
-    __shared__ __attribute__((aligned(16))) T sKa[64 * D];
-    __shared__ __attribute__((aligned(16))) T sKt[64 * D];
-    __shared__ __attribute__((aligned(16))) T sVa[64 * D];
+    __shared__ __attribute__((aligned(16))) T sKa[2][KT * D];
+    __shared__ __attribute__((aligned(16))) T sKt[2][KT * D];
+    __shared__ __attribute__((aligned(16))) T sVa[2][KT * D];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
@@ -410,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int kvh = h / a.group;
     const BwdSeq sq = bwd_seq(a, b);
     const int L = sq.L;
-    const int q0 = qt * 128;
+    const int q0 = qt * (32 * NW);
     if (q0 >= L) return;  // whole workgroup
     const int qw0 = q0 + 32 * w;
     const bool active = qw0 < L;
@@ -421,6 +508,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
     const T* Kg = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)kvh * a.ks[2];
     const T* Vg = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)kvh * a.vs[2];
+
+    // ---- staging: NKI items per thread of each key tile; rows past the end re-read the
+    // last row (finite, masked below)
+    StageItem pre[NKI];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < NKI; ++j) {
+            const int it = (tid + j * NT) % KITEMS;  // spare threads load a duplicate, never stored
+            const int r = it / CPR, c = (it % CPR) * 8;
+            const int kr = min(k0 + r, L - 1);
+            stage_load<T, PAIR>(pre[j], Kg + (int64_t)kr * a.ks[1], Vg + (int64_t)kr * a.vs[1],
+                                Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, c, HALF);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < NKI; ++j) {
+            const int it = tid + j * NT;
+            if (KITEMS % NT == 0 || it < KITEMS) {
+                const int r = it / CPR, c = (it % CPR) * 8;
+                u32x4 px, py;
+                stage_rotate<T, PAIR>(pre[j], px, py);
+                stage_store2<T, D>(sKa[buf], sKt[buf], r, c, px, py);
+                const int c0 = c / 8, c1 = (c + HALF) / 8;
+                *reinterpret_cast<u32x4*>(&sVa[buf][r * D + 8 * (c0 ^ swz_row(r))]) = pre[j].b0;
+                *reinterpret_cast<u32x4*>(&sVa[buf][r * D + 8 * (c1 ^ swz_row(r))]) = pre[j].b1;
+            }
+        }
+    };
 
     // ---- this lane's query row: rotated Q' and dO as B operands (column n = query, k = d)
     u32x4 qb[NS], db[NS];
@@ -442,6 +558,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     const float lse2 = a.lse[(int64_t)h * a.lse_stride + sq.tok + qrow] * kLog2e;
     const float del = a.delta[(int64_t)h * a.lse_stride + sq.tok + qrow];
+    // complete these loads here: otherwise the loop's first use would wait for every load
+    // issued after them, the prefetch included
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(db[s]));
+    asm volatile("" ::"v"(del));
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -451,45 +572,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
     const int pr = pi_row(n), fr = swz_row(pr);
-    const int q_hi = min(q0 + 128, L);
+    const int q_hi = min(q0 + 32 * NW, L);
     const int kend = a.causal ? q_hi : L;
-    const int n_kt = (kend + 63) / 64;
+    const int n_kt = (kend + KT - 1) / KT;
     const int wave_kend = a.causal ? min(qw0 + 32, L) : L;
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int k0 = kt * 64;
-        __syncthreads();  // the previous tile's LDS reads are done
-        // ---- stage K' (rotated; row and transposing copies) and V rows; rows past the end
-        // re-read the last row (finite, masked below)
-#pragma unroll
-        for (int j = 0; j < NKI; ++j) {
-            const int it = tid + j * 256;
-            if (KITEMS % 256 == 0 || it < KITEMS) {
-                const int r = it / (D / 16), c = (it % (D / 16)) * 8;
-                const int kr = min(k0 + r, L - 1);
-                const T* kp = Kg + (int64_t)kr * a.ks[1];
-                const T* vp = Vg + (int64_t)kr * a.vs[1];
-                float x[8], y[8];
-                unpack<T>(load_chunk<T>(kp + c), x);
-                unpack<T>(load_chunk<T>(kp + c + HALF), y);
-                rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, c, HALF);
-                const u32x4 v0 = load_chunk<T>(vp + c).w, v1 = load_chunk<T>(vp + c + HALF).w;
-                const int c0 = c / 8, c1 = (c + HALF) / 8;
-                const u32x4 px = pack<T>(x).w, py = pack<T>(y).w;
-                *reinterpret_cast<u32x4*>(&sKa[r * D + 8 * (c0 ^ swz_row(r))]) = px;
-                *reinterpret_cast<u32x4*>(&sKa[r * D + 8 * (c1 ^ swz_row(r))]) = py;
-                *reinterpret_cast<u32x4*>(&sKt[r * D + 8 * (c0 ^ swz_tr(r))]) = px;
-                *reinterpret_cast<u32x4*>(&sKt[r * D + 8 * (c1 ^ swz_tr(r))]) = py;
-                *reinterpret_cast<u32x4*>(&sVa[r * D + 8 * (c0 ^ swz_row(r))]) = v0;
-                *reinterpret_cast<u32x4*>(&sVa[r * D + 8 * (c1 ^ swz_row(r))]) = v1;
-            }
-        }
-        __syncthreads();
-        if (!active || k0 >= wave_kend) continue;  // wave-uniform
+    // key kk of this lane's row is kept iff kk <= kmax
+    const int kmax = a.causal ? min(qi, L - 1) : L - 1;
 
-        u32x4 dsk[2][2];
+    load_tile(0);
+    for (int kt = 0, buf = 0; kt < n_kt; ++kt, buf ^= 1) {
+        const int k0 = kt * KT;
+        store_tile(buf);
+        __syncthreads();  // tile visible; every read of this buffer two tiles back is done
+        // after the last tile this reloads it (never stored): no branch around the loads
+        load_tile(min(k0 + KT, (n_kt - 1) * KT));
+        if (!active || k0 >= wave_kend) continue;  // wave-uniform
+        const T* ka = sKa[buf];
+        const T* ktr = sKt[buf];
+        const T* va = sVa[buf];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < NB; ++blk) {
             // ---- S^T and dP^T: lane (n, hh) gets query qi against keys k0 + 32*blk + 16hh + i
             const int rr = blk * 32 + pr;
             f32x16 sacc, dpacc;
@@ -498,39 +601,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int off = rr * D + 8 * ((2 * s + hh) ^ fr);
-                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sKa[off]), qb[s], sacc);
-                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&sVa[off]), db[s], dpacc);
+                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&ka[off]), qb[s], sacc);
+                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&va[off]), db[s], dpacc);
             }
+            const int thr = kmax - (k0 + 32 * blk + 16 * hh);  // key ... + i is masked iff i > thr
+            u32x4 dsk[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 float ds[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int i = 8 * s + j;
-                    const int kk = k0 + 32 * blk + 16 * hh + i;
                     float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lse2));
-                    if ((a.causal && kk > qi) || kk >= L) pv = 0.0f;
+                    if (i > thr) pv = 0.0f;
                     ds[j] = pv * (dpacc[i] - del);
                 }
-                dsk[blk][s] = pack<T>(ds).w;
+                dsk[s] = pack<T>(ds).w;
             }
-        }
-        // ---- dQ'^T += K'^T dS^T
+            // ---- dQ'^T += K'^T dS^T
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
                     const int e = mb * 32 + tr_col;
                     const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
-                    const i16x4 lo = bwd_tr16(&sKt[r * D + sw]);
-                    const i16x4 hi = bwd_tr16(&sKt[(r + 4) * D + sw]);
+                    const i16x4 lo = bwd_tr16(&ktr[r * D + sw]);
+                    const i16x4 hi = bwd_tr16(&ktr[(r + 4) * D + sw]);
                     dqacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
                                                                                                 6, 7)),
-                                             dsk[blk][s], dqacc[mb]);
+                                             dsk[s], dqacc[mb]);
                 }
+        }
     }
 
     // ---- epilogue: dq = M^T (s * dQ')
@@ -541,13 +643,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ============================================================================ launch
+#ifndef BWD_DQ_NW
+#define BWD_DQ_NW 8
+#endif
+#ifndef BWD_DQ_KT
+#define BWD_DQ_KT 64
+#endif
 template <typename T, int D, int PAIR>
 static void launch_bwd_typed(const BwdArgs& a, int maxlen, hipStream_t stream) {
+    constexpr int NW = BWD_DQ_NW, KT = BWD_DQ_KT;
     const int64_t dthreads = (int64_t)a.rows * a.hq * (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream, a);
-    const unsigned tiles = (unsigned)((maxlen + 127) / 128);
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3(tiles, a.hkv, a.batch), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR>), dim3(tiles, a.hq, a.batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3((unsigned)((maxlen + 127) / 128), a.hkv, a.batch),
+                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR, NW, KT>), dim3((unsigned)((maxlen + 32 * NW - 1) / (32 * NW)), a.hq,
+                                                                 a.batch),
+                       dim3(NW * 64), 0, stream, a);
 }
 
 template <typename T, int D>
