@@ -46,8 +46,23 @@ struct BwdArgs {
     int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // {batch, token, head}
     int32_t batch, hq, hkv, group, seqlen, table_seq_rows, lse_stride, causal;
     int32_t rows;                // query rows in total (dense batch*seqlen, varlen ntokens)
+    int32_t kv_tiles, q_tiles;   // 128-key tiles (dK/dV grid) and query tiles (dQ grid) per sequence
     float scale, scale_log2;
 };
+
+// Workgroups go to the 8 XCDs round robin by linear id.  The workgroups of one group
+// (those reading the same rows: one (sequence, kv head)) are kept on one XCD and
+// dispatched back to back, so they share that XCD's L2; item = rank within the group.
+__device__ __forceinline__ void xcd_grouped(int id, int per_group, int ngroups, int& grp, int& item) {
+    if ((ngroups & 7) == 0) {
+        const int slot = id >> 3;
+        grp = (id & 7) + 8 * (slot / per_group);
+        item = slot % per_group;
+    } else {
+        grp = id / per_group;
+        item = id - grp * per_group;
+    }
+}
 
 template <typename T> struct BMma;
 template <> struct BMma<__bf16> {
@@ -69,10 +84,22 @@ __device__ __forceinline__ i16x4 bwd_tr16(const void* p) {
 }
 // MFMA row m holds row pi(m) of a 32-row block: lane half h then holds rows 16h .. 16h+15
 __device__ __forceinline__ int pi_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
-// chunk swizzles: for the row reads (8 lanes = rows {0..3, 16..19} + 4k) and for the
-// transposing reads (4 consecutive rows x 2 chunks per 16 lanes)
-__device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 4) & 1) << 2); }
-__device__ __forceinline__ int swz_tr(int r) { return 2 * (r & 3); }
+// LDS tiles hold rows at pitch D (no padding); 16-byte chunk c of row r sits at chunk
+// position c ^ f(r).  LDS has 64 banks of 4 bytes: a 16-byte access is served 16 lanes
+// at a time and an 8-byte access 32 lanes at a time, so each such group must touch 16
+// distinct 16-byte bank groups.
+//   swz_row: copies read as MFMA operands row by row; a 16-lane group reads rows
+//            {0..3, 16..19, 4..7, 20..23} (+8) of the pi order at one chunk column.
+//   swz_tr:  copies read by ds_read_b64_tr_b16; 32 lanes read 4 consecutive rows x 4
+//            chunks.  Depends on r % 4 only.
+template <int D> __device__ __forceinline__ int swz_row(int r) {
+    if (D == 128) return (r & 7) | (((r >> 4) & 1) << 3);
+    return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);  // D = 64: two rows per 256 bytes
+}
+template <int D> __device__ __forceinline__ int swz_tr(int r) {
+    if (D == 128) return 4 * (r & 3);
+    return 4 * ((r >> 1) & 1);
+}
 
 struct BwdSeq {
     int L;
@@ -270,15 +297,24 @@ __device__ __forceinline__ void stage_rotate(const StageItem& s, u32x4& px, u32x
     py = pack<T>(y).w;
 }
 
-// Writes chunk pair (c/8, (c+D/2)/8) of row r into a row-read copy and a transposing-read
-// copy of an LDS tile (different XOR swizzles).
+// Writes chunk pair (c/8, (c+D/2)/8) of row r (x, y) into one LDS copy.  Staging items
+// run along rows (D/16 items per row), so a 16-lane store group covers 2 (D = 128) or 4
+// (D = 64) rows; on some of them the two chunks are stored in the other order, which
+// makes each store instruction's group touch 16 distinct bank groups.
+template <typename T, int D, bool TR>
+__device__ __forceinline__ void stage_store1(T* tile, int r, int c, const u32x4& x, const u32x4& y) {
+    const int f = TR ? swz_tr<D>(r) : swz_row<D>(r);
+    const bool sw = D == 128 ? (r & 1) != 0 : (!TR && ((r >> 1) & 1) != 0);
+    const int c0 = c / 8, c1 = (c + D / 2) / 8;
+    const int ca = sw ? c1 : c0, cb = sw ? c0 : c1;
+    *reinterpret_cast<u32x4*>(&tile[r * D + 8 * (ca ^ f)]) = sw ? y : x;
+    *reinterpret_cast<u32x4*>(&tile[r * D + 8 * (cb ^ f)]) = sw ? x : y;
+}
+// The same chunk pair into a row-read copy and a transposing-read copy.
 template <typename T, int D>
 __device__ __forceinline__ void stage_store2(T* ta, T* tt, int r, int c, const u32x4& x, const u32x4& y) {
-    const int c0 = c / 8, c1 = (c + D / 2) / 8;
-    *reinterpret_cast<u32x4*>(&ta[r * D + 8 * (c0 ^ swz_row(r))]) = x;
-    *reinterpret_cast<u32x4*>(&ta[r * D + 8 * (c1 ^ swz_row(r))]) = y;
-    *reinterpret_cast<u32x4*>(&tt[r * D + 8 * (c0 ^ swz_tr(r))]) = x;
-    *reinterpret_cast<u32x4*>(&tt[r * D + 8 * (c1 ^ swz_tr(r))]) = y;
+    stage_store1<T, D, false>(ta, r, c, x, y);
+    stage_store1<T, D, true>(tt, r, c, x, y);
 }
 
 // ============================================================================ dk, dv
@@ -299,11 +335,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    int grp, tile;
+    xcd_grouped(blockIdx.x, a.kv_tiles, a.hkv * a.batch, grp, tile);
+    const int kvh = grp % a.hkv;
+    const int b = grp / a.hkv;
     const BwdSeq sq = bwd_seq(a, b);
     const int L = sq.L;
-    const int k0 = blockIdx.x * 128;
+    const int k0 = tile * 128;
     if (k0 >= L) return;  // whole workgroup
     const int kw0 = k0 + 32 * w;
     const bool active = kw0 < L;
@@ -377,27 +415,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) dvacc[mb][i] = dkacc[mb][i] = 0.0f;
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
-    const int pr = pi_row(n), fr = swz_row(pr);
+    const int pr = pi_row(n), fr = swz_row<D>(pr);
     const int mykey = kw0 + n;
     // P of (query qi, this key) is kept iff qi >= qmin
     const int qmin = mykey >= L ? (1 << 30) : (a.causal ? mykey : -(1 << 30));
     const int q_begin = a.causal ? k0 : 0;
 
-    // blocks in order (q head of the group, 32-row query block)
-    int ld_hi = 0, ld_q0 = q_begin;
+    // blocks in order: 32-row query blocks from the last one down, and the group's q heads
+    // within each; the workgroups of all key tiles of this (sequence, kv head) start
+    // together at the last block and stay in step, reading the same rows at the same time
+    const int q_last = q_begin + ((L - 1 - q_begin) >> 5) * 32;
+    int ld_hi = 0, ld_q0 = q_last;
     load_block(ld_hi, ld_q0);
     for (int buf = 0;; buf ^= 1) {
         const int q0 = ld_q0;
         store_block(buf, q0);
         __syncthreads();  // block visible; every read of this buffer two blocks back is done
-        ld_q0 += 32;
-        if (ld_q0 >= L) {
-            ld_q0 = q_begin;
-            ++ld_hi;
+        if (++ld_hi == a.group) {
+            ld_hi = 0;
+            ld_q0 -= 32;
         }
-        const bool more = ld_hi < a.group;
-        // after the last block this reloads the first one (never stored): no branch
-        load_block(more ? ld_hi : 0, ld_q0);
+        const bool more = ld_q0 >= q_begin;
+        // after the last block this reloads a valid one (never stored): no branch
+        load_block(more ? ld_hi : 0, more ? ld_q0 : q_begin);
         if (active && !(a.causal && q0 + 31 < kw0)) {  // wave-uniform
             const T* qa = sQa[buf];
             const T* qt = sQt[buf];
@@ -447,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
                 for (int s = 0; s < 2; ++s) {
                     const int r = 16 * hh + 8 * s + tr_row;  // r % 4 == tr_row
                     const int e = mb * 32 + tr_col;
-                    const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
+                    const int sw = 8 * ((e >> 3) ^ swz_tr<D>(tr_row)) + (e & 7);
                     const i16x4 dlo = bwd_tr16(&dt[r * D + sw]);
                     const i16x4 dhi = bwd_tr16(&dt[(r + 4) * D + sw]);
                     dvacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4,
@@ -491,10 +531,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
-    const int qt = gridDim.x - 1 - blockIdx.x;  // longest query tiles first
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
-    const int kvh = h / a.group;
+    // group = (sequence, kv head); within it: query tiles longest first, the q heads of the
+    // kv head next to each other (they read the same K/V tiles in the same order)
+    int grp, item;
+    xcd_grouped(blockIdx.x, a.q_tiles * a.group, a.hkv * a.batch, grp, item);
+    const int kvh = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const int qt = a.q_tiles - 1 - item / a.group;
+    const int h = kvh * a.group + item % a.group;
     const BwdSeq sq = bwd_seq(a, b);
     const int L = sq.L;
     const int q0 = qt * (32 * NW);
@@ -531,9 +575,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 u32x4 px, py;
                 stage_rotate<T, PAIR>(pre[j], px, py);
                 stage_store2<T, D>(sKa[buf], sKt[buf], r, c, px, py);
-                const int c0 = c / 8, c1 = (c + HALF) / 8;
-                *reinterpret_cast<u32x4*>(&sVa[buf][r * D + 8 * (c0 ^ swz_row(r))]) = pre[j].b0;
-                *reinterpret_cast<u32x4*>(&sVa[buf][r * D + 8 * (c1 ^ swz_row(r))]) = pre[j].b1;
+                stage_store1<T, D, false>(sVa[buf], r, c, pre[j].b0, pre[j].b1);
             }
         }
     };
@@ -571,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) dqacc[mb][i] = 0.0f;
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
-    const int pr = pi_row(n), fr = swz_row(pr);
+    const int pr = pi_row(n), fr = swz_row<D>(pr);
     const int q_hi = min(q0 + 32 * NW, L);
     const int kend = a.causal ? q_hi : L;
     const int n_kt = (kend + KT - 1) / KT;
@@ -625,7 +667,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 for (int s = 0; s < 2; ++s) {
                     const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
                     const int e = mb * 32 + tr_col;
-                    const int sw = 8 * ((e >> 3) ^ (2 * tr_row)) + (e & 7);
+                    const int sw = 8 * ((e >> 3) ^ swz_tr<D>(tr_row)) + (e & 7);
                     const i16x4 lo = bwd_tr16(&ktr[r * D + sw]);
                     const i16x4 hi = bwd_tr16(&ktr[(r + 4) * D + sw]);
                     dqacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
@@ -654,11 +696,13 @@ static void launch_bwd_typed(const BwdArgs& a, int maxlen, hipStream_t stream) {
     constexpr int NW = BWD_DQ_NW, KT = BWD_DQ_KT;
     const int64_t dthreads = (int64_t)a.rows * a.hq * (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3((unsigned)((maxlen + 127) / 128), a.hkv, a.batch),
-                       dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR, NW, KT>), dim3((unsigned)((maxlen + 32 * NW - 1) / (32 * NW)), a.hq,
-                                                                 a.batch),
-                       dim3(NW * 64), 0, stream, a);
+    BwdArgs g = a;
+    g.kv_tiles = (maxlen + 127) / 128;
+    g.q_tiles = (maxlen + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3((unsigned)(g.kv_tiles * a.hkv * a.batch)), dim3(256), 0,
+                       stream, g);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR, NW, KT>), dim3((unsigned)(g.q_tiles * a.hq * a.batch)), dim3(NW * 64),
+                       0, stream, g);
 }
 
 template <typename T, int D>
