@@ -18,13 +18,18 @@
 //     lane half with 16 consecutive queries of one key), then dV^T += dO^T P and
 //     dK'^T += Q'^T dS with the transposing LDS read (ds_read_b64_tr_b16) supplying
 //     dO^T and Q'^T.
-//   * bwd_dq_kernel: a workgroup of 4 waves owns 128 query rows of one (sequence, q head);
+//   * bwd_dq_kernel: a workgroup of 8 waves owns 256 query rows of one (sequence, q head);
 //     each wave keeps its 32 rows' Q' and dO as B operands and, per 64-key tile staged in
 //     LDS (K' rotated while staging, V), forms S^T, dP^T and dS^T and accumulates
 //     dQ'^T += K'^T dS^T (K'^T by the transposing read).
-// Each LDS tile read both ways is stored twice with different 16-byte chunk XOR swizzles
-// (row reads: pi-row groups, transposing reads: 4-row groups), both bank-conflict free.
-// The epilogues apply M^T (the transposed Rope op) to dq' and dk' before the stores.
+// An LDS tile read both ways is stored twice: rows in the pi order for the row reads and
+// in natural order for the transposing reads, each at a padded pitch (bank-conflict free
+// reads, constant read offsets).  Each kernel loads the next block into registers while
+// it computes the current one (LDS double-buffered, one barrier per block); the
+// workgroups that read the same rows run on one XCD in step.  The epilogues apply M^T
+// (the transposed Rope op) to dq' and dk' before the stores.
+#include <type_traits>
+
 #include "common.h"
 
 namespace ropefa {
@@ -84,22 +89,19 @@ __device__ __forceinline__ i16x4 bwd_tr16(const void* p) {
 }
 // MFMA row m holds row pi(m) of a 32-row block: lane half h then holds rows 16h .. 16h+15
 __device__ __forceinline__ int pi_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
-// LDS tiles hold rows at pitch D (no padding); 16-byte chunk c of row r sits at chunk
-// position c ^ f(r).  LDS has 64 banks of 4 bytes: a 16-byte access is served 16 lanes
-// at a time and an 8-byte access 32 lanes at a time, so each such group must touch 16
-// distinct 16-byte bank groups.
-//   swz_row: copies read as MFMA operands row by row; a 16-lane group reads rows
-//            {0..3, 16..19, 4..7, 20..23} (+8) of the pi order at one chunk column.
-//   swz_tr:  copies read by ds_read_b64_tr_b16; 32 lanes read 4 consecutive rows x 4
-//            chunks.  Depends on r % 4 only.
-template <int D> __device__ __forceinline__ int swz_row(int r) {
-    if (D == 128) return (r & 7) | (((r >> 4) & 1) << 3);
-    return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);  // D = 64: two rows per 256 bytes
-}
-template <int D> __device__ __forceinline__ int swz_tr(int r) {
-    if (D == 128) return 4 * (r & 3);
-    return 4 * ((r >> 1) & 1);
-}
+__device__ __forceinline__ int pi_inv(int r) { return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 3) << 3); }
+
+// LDS tiles.  A tile read as MFMA A operands row by row is stored with its rows in the pi
+// order (row m of each 32-row block holds row pi(m)), pitch D + 8: lane n reads row n, so
+// every read is the lane's base plus a constant, and a 16-lane group of 16-byte reads
+// (rows n .. n+15) starts on 16 distinct 4-bank groups (LDS: 64 banks of 4 bytes).  A tile
+// read by ds_read_b64_tr_b16 keeps the natural row order at pitch D + 32: the 32 lanes of
+// such a read cover 4 consecutive rows x 64 bytes, which then fall in 4 distinct 16-bank
+// quarters.  Stores are at most 2-way bank conflicted.
+template <int D> struct BwdLds {
+    static constexpr int PA = D + 8;   // row-read copies
+    static constexpr int PT = D + 32;  // transposing-read copies
+};
 
 struct BwdSeq {
     int L;
@@ -138,22 +140,37 @@ __device__ __forceinline__ BwdSeq bwd_seq(const BwdArgs& a, int b) {
     return s;
 }
 
-// The Rope op (M) on a chunk pair: x = columns d..d+7, y = columns d+D/2..d+D/2+7 of one row.
+// The Rope op (M) of the fused forward on a packed chunk pair: x = columns d..d+7, y =
+// columns d+D/2..d+D/2+7 of one row, rounded once to T.  Rotate-half uses the table's first
+// half only (columns d..d+7 for both halves), as the forward does; interleaved uses both.
 template <typename T, int PAIR>
-__device__ __forceinline__ void rope_fwd_pair(float (&x)[8], float (&y)[8], const T* crow, const T* srow, int d,
-                                              int half) {
-    if (PAIR == 0) return;
-    float c0[8], s0[8], c1[8], s1[8];
-    unpack<T>(load_chunk<T>(crow + d), c0);
-    unpack<T>(load_chunk<T>(srow + d), s0);
-    unpack<T>(load_chunk<T>(crow + d + half), c1);
-    unpack<T>(load_chunk<T>(srow + d + half), s1);
+__device__ __forceinline__ void rope_fwd_packed(u32x4& x, u32x4& y, const u32x4& c0, const u32x4& s0, const u32x4& c1,
+                                                const u32x4& s1) {
     if (PAIR == 1) {
-        rotate_pair(x, y, c0, s0, c1, s1);
-    } else {
-        rotate_interleaved(x, c0, s0);
-        rotate_interleaved(y, c1, s1);
+        u32x4 xo, yo;
+        rotate_pair_packed<T>(x, y, c0, s0, xo, yo);
+        x = xo;
+        y = yo;
+    } else if (PAIR == 2) {
+        x = rotate_interleaved_packed<T>(x, c0, s0);
+        y = rotate_interleaved_packed<T>(y, c1, s1);
     }
+}
+
+// Loads chunk pair (d, d + D/2) of row p and rotates it with the row's table values.
+template <typename T, int PAIR>
+__device__ __forceinline__ void load_rotated_pair(const T* p, const T* crow, const T* srow, int d, int half, u32x4& x,
+                                                  u32x4& y) {
+    x = load_chunk<T>(p + d).w;
+    y = load_chunk<T>(p + d + half).w;
+    if (PAIR == 0) return;
+    const u32x4 c0 = load_chunk<T>(crow + d).w, s0 = load_chunk<T>(srow + d).w;
+    u32x4 c1 = c0, s1 = s0;
+    if (PAIR == 2) {
+        c1 = load_chunk<T>(crow + d + half).w;
+        s1 = load_chunk<T>(srow + d + half).w;
+    }
+    rope_fwd_packed<T, PAIR>(x, y, c0, s0, c1, s1);
 }
 
 // ============================================================================ delta
@@ -198,25 +215,24 @@ __device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], floa
 #pragma unroll
         for (int i = 0; i < 16; ++i) g[mb][i] = acc[mb][i] * scale;
     if (PAIR == 1) {
-        // M^T for pairs (j, j + D/2): g'_j = c_j g_j + s_{j+D/2} g_{j+D/2}, g'_{j+D/2} = c_{j+D/2} g_{j+D/2} - s_j g_j
+        // M^T for pairs (j, j + D/2) with the table's first half (the forward's M):
+        //   g'_j = c_j g_j + s_j g_{j+D/2},  g'_{j+D/2} = c_j g_{j+D/2} - s_j g_j
 #pragma unroll
         for (int mb = 0; mb < D / 64; ++mb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d0 = mb * 32 + 8 * q4 + 4 * hh;
-                float c0[4], s0[4], c1[4], s1[4];
+                float c0[4], s0[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     c0[e] = (float)crow[d0 + e];
                     s0[e] = (float)srow[d0 + e];
-                    c1[e] = (float)crow[d0 + HALF + e];
-                    s1[e] = (float)srow[d0 + HALF + e];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x = g[mb][4 * q4 + e], y = g[mb + D / 64][4 * q4 + e];
-                    g[mb][4 * q4 + e] = __builtin_fmaf(x, c0[e], __fmul_rn(y, s1[e]));
-                    g[mb + D / 64][4 * q4 + e] = __builtin_fmaf(y, c1[e], -__fmul_rn(x, s0[e]));
+                    g[mb][4 * q4 + e] = __builtin_fmaf(x, c0[e], __fmul_rn(y, s0[e]));
+                    g[mb + D / 64][4 * q4 + e] = __builtin_fmaf(y, c0[e], -__fmul_rn(x, s0[e]));
                 }
             }
     } else if (PAIR == 2) {
@@ -251,10 +267,10 @@ __device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], floa
 // ============================================================================ staging
 // One staging item: the 8-element chunks at columns c and c + D/2 of one row of two
 // tensors (the first is rotated, the second copied) and, when rotating, the row's table
-// chunks at the same columns.  Loaded one block ahead into registers, rotated and written
-// to LDS at the start of the next block.
+// chunks (rotate-half: columns c..c+7; interleaved: both).  Loaded one block ahead into
+// registers, rotated and written to LDS at the start of the next block.
 struct StageItem {
-    u32x4 a0, a1, b0, b1, c0, c1, s0, s1;
+    u32x4 a0, a1, b0, b1, c0, s0, c1, s1;
 };
 
 template <typename T, int PAIR>
@@ -266,55 +282,35 @@ __device__ __forceinline__ void stage_load(StageItem& s, const T* arow, const T*
     s.b1 = load_chunk<T>(brow + c + half).w;
     if (PAIR != 0) {
         s.c0 = load_chunk<T>(crow + c).w;
-        s.c1 = load_chunk<T>(crow + c + half).w;
         s.s0 = load_chunk<T>(srow + c).w;
+    }
+    if (PAIR == 2) {
+        s.c1 = load_chunk<T>(crow + c + half).w;
         s.s1 = load_chunk<T>(srow + c + half).w;
     }
 }
 
-// The Rope op (M) on a staged item's first tensor, rounded once to T.
+// The Rope op (M) on a staged item's first tensor.
 template <typename T, int PAIR>
 __device__ __forceinline__ void stage_rotate(const StageItem& s, u32x4& px, u32x4& py) {
-    if (PAIR == 0) {
-        px = s.a0;
-        py = s.a1;
-        return;
-    }
-    float x[8], y[8], c0[8], s0[8], c1[8], s1[8];
-    unpack<T>(Chunk8<T>{s.a0}, x);
-    unpack<T>(Chunk8<T>{s.a1}, y);
-    unpack<T>(Chunk8<T>{s.c0}, c0);
-    unpack<T>(Chunk8<T>{s.s0}, s0);
-    unpack<T>(Chunk8<T>{s.c1}, c1);
-    unpack<T>(Chunk8<T>{s.s1}, s1);
-    if (PAIR == 1) {
-        rotate_pair(x, y, c0, s0, c1, s1);
-    } else {
-        rotate_interleaved(x, c0, s0);
-        rotate_interleaved(y, c1, s1);
-    }
-    px = pack<T>(x).w;
-    py = pack<T>(y).w;
+    px = s.a0;
+    py = s.a1;
+    rope_fwd_packed<T, PAIR>(px, py, s.c0, s.s0, s.c1, s.s1);
 }
 
-// Writes chunk pair (c/8, (c+D/2)/8) of row r (x, y) into one LDS copy.  Staging items
-// run along rows (D/16 items per row), so a 16-lane store group covers 2 (D = 128) or 4
-// (D = 64) rows; on some of them the two chunks are stored in the other order, which
-// makes each store instruction's group touch 16 distinct bank groups.
-template <typename T, int D, bool TR>
-__device__ __forceinline__ void stage_store1(T* tile, int r, int c, const u32x4& x, const u32x4& y) {
-    const int f = TR ? swz_tr<D>(r) : swz_row<D>(r);
-    const bool sw = D == 128 ? (r & 1) != 0 : (!TR && ((r >> 1) & 1) != 0);
-    const int c0 = c / 8, c1 = (c + D / 2) / 8;
-    const int ca = sw ? c1 : c0, cb = sw ? c0 : c1;
-    *reinterpret_cast<u32x4*>(&tile[r * D + 8 * (ca ^ f)]) = sw ? y : x;
-    *reinterpret_cast<u32x4*>(&tile[r * D + 8 * (cb ^ f)]) = sw ? x : y;
-}
-// The same chunk pair into a row-read copy and a transposing-read copy.
+// Writes chunk pair (c, c + D/2) (element columns) of row r of a 32-row-block tile: x, y
+// into the row-read copy (pi order) and/or the transposing-read copy (natural order).
 template <typename T, int D>
-__device__ __forceinline__ void stage_store2(T* ta, T* tt, int r, int c, const u32x4& x, const u32x4& y) {
-    stage_store1<T, D, false>(ta, r, c, x, y);
-    stage_store1<T, D, true>(tt, r, c, x, y);
+__device__ __forceinline__ void store_rowcopy(T* ta, int r, int c, const u32x4& x, const u32x4& y) {
+    T* p = ta + ((r & ~31) + pi_inv(r & 31)) * BwdLds<D>::PA + c;
+    *reinterpret_cast<u32x4*>(p) = x;
+    *reinterpret_cast<u32x4*>(p + D / 2) = y;
+}
+template <typename T, int D>
+__device__ __forceinline__ void store_trcopy(T* tt, int r, int c, const u32x4& x, const u32x4& y) {
+    T* p = tt + r * BwdLds<D>::PT + c;
+    *reinterpret_cast<u32x4*>(p) = x;
+    *reinterpret_cast<u32x4*>(p + D / 2) = y;
 }
 
 // ============================================================================ dk, dv
@@ -326,10 +322,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int QITEMS = 32 * CPR;   // staging items of a 32-row block (<= 256)
     constexpr float kLog2e = 1.4426950408889634f;
     // double-buffered: block i is written to buffer i & 1 while block i - 1 is read
-    __shared__ __attribute__((aligned(16))) T sQa[2][32 * D];
-    __shared__ __attribute__((aligned(16))) T sQt[2][32 * D];
-    __shared__ __attribute__((aligned(16))) T sDa[2][32 * D];
-    __shared__ __attribute__((aligned(16))) T sDt[2][32 * D];
+    constexpr int PA = BwdLds<D>::PA, PT = BwdLds<D>::PT;
+    __shared__ __attribute__((aligned(16))) T sQa[2][32 * PA];
+    __shared__ __attribute__((aligned(16))) T sQt[2][32 * PT];
+    __shared__ __attribute__((aligned(16))) T sDa[2][32 * PA];
+    __shared__ __attribute__((aligned(16))) T sDt[2][32 * PT];
     __shared__ __attribute__((aligned(16))) float sL[2][32];
     __shared__ __attribute__((aligned(16))) float sDel[2][32];
 
@@ -354,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     // ---- staging role: item (row sr, chunk pair sc) of each 32-row block; rows past the
     // end re-read the last row (finite values; their P is exactly 0 through lse = +inf)
-    const bool stager = tid < QITEMS;
+    const bool stager = QITEMS >= 256 || tid < QITEMS;
     const int sr = (tid % QITEMS) / CPR, sc = (tid % CPR) * 8;
     // Every thread issues its loads unconditionally (no branch around a load, so no wait
     // is forced at a join); the loaded values are only used at the next block's store.
@@ -374,8 +371,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         if (stager) {
             u32x4 px, py;
             stage_rotate<T, PAIR>(pre, px, py);
-            stage_store2<T, D>(sQa[buf], sQt[buf], sr, sc, px, py);
-            stage_store2<T, D>(sDa[buf], sDt[buf], sr, sc, pre.b0, pre.b1);
+            store_rowcopy<T, D>(sQa[buf], sr, sc, px, py);
+            store_trcopy<T, D>(sQt[buf], sr, sc, px, py);
+            store_rowcopy<T, D>(sDa[buf], sr, sc, pre.b0, pre.b1);
+            store_trcopy<T, D>(sDt[buf], sr, sc, pre.b0, pre.b1);
         }
         if (tid < 32) {
             // rows past the end get lse = +inf: their P is exactly 0
@@ -391,15 +390,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         const T* kp = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)key * a.ks[1] + (int64_t)kvh * a.ks[2];
         const T* vp = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)key * a.vs[1] + (int64_t)kvh * a.vs[2];
 #pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            const int d = 16 * s + 8 * hh;
-            float x[8], y[8];
-            unpack<T>(load_chunk<T>(kp + d), x);
-            unpack<T>(load_chunk<T>(kp + d + HALF), y);
-            rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)key * D, Sg + (int64_t)key * D, d, HALF);
-            kb[s] = pack<T>(x).w;
-            kb[s + NS / 2] = pack<T>(y).w;
-        }
+        for (int s = 0; s < NS / 2; ++s)
+            load_rotated_pair<T, PAIR>(kp, Cg + (int64_t)key * D, Sg + (int64_t)key * D, 16 * s + 8 * hh, HALF, kb[s],
+                                       kb[s + NS / 2]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
         // complete these loads here: otherwise the loop's first use would wait for every
@@ -415,7 +408,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) dvacc[mb][i] = dkacc[mb][i] = 0.0f;
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
-    const int pr = pi_row(n), fr = swz_row<D>(pr);
     const int mykey = kw0 + n;
     // P of (query qi, this key) is kept iff qi >= qmin
     const int qmin = mykey >= L ? (1 << 30) : (a.causal ? mykey : -(1 << 30));
@@ -444,14 +436,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
             const T* da = sDa[buf];
             const T* dt = sDt[buf];
             // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i
+            // every A operand is read before the first product, so the products do not wait
+            // on one LDS round trip each
+            u32x4 aq[NS], ad[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int off = n * PA + 16 * s + 8 * hh;
+                aq[s] = *reinterpret_cast<const u32x4*>(&qa[off]);
+                ad[s] = *reinterpret_cast<const u32x4*>(&da[off]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 sacc, dpacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int off = pr * D + 8 * ((2 * s + hh) ^ fr);
-                sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&qa[off]), kb[s], sacc);
-                dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&da[off]), vb[s], dpacc);
+                sacc = BMma<T>::run(aq[s], kb[s], sacc);
+                dpacc = BMma<T>::run(ad[s], vb[s], dpacc);
             }
             const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
             float lv[16], dl[16];
@@ -466,35 +467,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
                 }
             }
             u32x4 pk[2], dsk[2];
+            auto probs = [&](auto masked) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float p[8], ds[8];
+                for (int s = 0; s < 2; ++s) {
+                    float p[8], ds[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 8 * s + j;
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv[i]));
-                    if (i < thr) pv = 0.0f;
-                    p[j] = pv;
-                    ds[j] = pv * (dpacc[i] - dl[i]);
+                    for (int j = 0; j < 8; ++j) {
+                        const int i = 8 * s + j;
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv[i]));
+                        if (decltype(masked)::value && i < thr) pv = 0.0f;
+                        p[j] = pv;
+                        ds[j] = pv * (dpacc[i] - dl[i]);
+                    }
+                    pk[s] = pack<T>(p).w;
+                    dsk[s] = pack<T>(ds).w;
                 }
-                pk[s] = pack<T>(p).w;
-                dsk[s] = pack<T>(ds).w;
-            }
+            };
+            // the mask matters only for blocks that reach this wave's keys (causal) or
+            // for keys past the end: a wave-uniform choice
+            if (kw0 + 31 >= L || (a.causal && q0 < kw0 + 31))
+                probs(std::true_type{});
+            else
+                probs(std::false_type{});
             // ---- dV^T += dO^T P,  dK'^T += Q'^T dS
 #pragma unroll
             for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const int r = 16 * hh + 8 * s + tr_row;  // r % 4 == tr_row
+                    const int r = 16 * hh + 8 * s + tr_row;
                     const int e = mb * 32 + tr_col;
-                    const int sw = 8 * ((e >> 3) ^ swz_tr<D>(tr_row)) + (e & 7);
-                    const i16x4 dlo = bwd_tr16(&dt[r * D + sw]);
-                    const i16x4 dhi = bwd_tr16(&dt[(r + 4) * D + sw]);
+                    const i16x4 dlo = bwd_tr16(&dt[r * PT + e]);
+                    const i16x4 dhi = bwd_tr16(&dt[(r + 4) * PT + e]);
                     dvacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4,
                                                                                                 5, 6, 7)),
                                              pk[s], dvacc[mb]);
-                    const i16x4 qlo = bwd_tr16(&qt[r * D + sw]);
-                    const i16x4 qhi = bwd_tr16(&qt[(r + 4) * D + sw]);
+                    const i16x4 qlo = bwd_tr16(&qt[r * PT + e]);
+                    const i16x4 qhi = bwd_tr16(&qt[(r + 4) * PT + e]);
                     dkacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4,
                                                                                                 5, 6, 7)),
                                              dsk[s], dkacc[mb]);
@@ -525,9 +533,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NKI = (KITEMS + NT - 1) / NT;
     constexpr int NB = KT / 32;       // 32-key blocks per tile
     constexpr float kLog2e = 1.4426950408889634f;
-    __shared__ __attribute__((aligned(16))) T sKa[2][KT * D];
-    __shared__ __attribute__((aligned(16))) T sKt[2][KT * D];
-    __shared__ __attribute__((aligned(16))) T sVa[2][KT * D];
+    constexpr int PA = BwdLds<D>::PA, PT = BwdLds<D>::PT;
+    __shared__ __attribute__((aligned(16))) T sKa[2][KT * PA];
+    __shared__ __attribute__((aligned(16))) T sKt[2][KT * PT];
+    __shared__ __attribute__((aligned(16))) T sVa[2][KT * PA];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
@@ -574,8 +583,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 const int r = it / CPR, c = (it % CPR) * 8;
                 u32x4 px, py;
                 stage_rotate<T, PAIR>(pre[j], px, py);
-                stage_store2<T, D>(sKa[buf], sKt[buf], r, c, px, py);
-                stage_store1<T, D, false>(sVa[buf], r, c, pre[j].b0, pre[j].b1);
+                store_rowcopy<T, D>(sKa[buf], r, c, px, py);
+                store_trcopy<T, D>(sKt[buf], r, c, px, py);
+                store_rowcopy<T, D>(sVa[buf], r, c, pre[j].b0, pre[j].b1);
             }
         }
     };
@@ -586,15 +596,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         const T* qp = reinterpret_cast<const T*>(a.q) + sq.bq + (int64_t)qrow * a.qs[1] + (int64_t)h * a.qs[2];
         const T* dp = reinterpret_cast<const T*>(a.dout) + sq.bdo + (int64_t)qrow * a.dos[1] + (int64_t)h * a.dos[2];
 #pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            const int d = 16 * s + 8 * hh;
-            float x[8], y[8];
-            unpack<T>(load_chunk<T>(qp + d), x);
-            unpack<T>(load_chunk<T>(qp + d + HALF), y);
-            rope_fwd_pair<T, PAIR>(x, y, Cg + (int64_t)qrow * D, Sg + (int64_t)qrow * D, d, HALF);
-            qb[s] = pack<T>(x).w;
-            qb[s + NS / 2] = pack<T>(y).w;
-        }
+        for (int s = 0; s < NS / 2; ++s)
+            load_rotated_pair<T, PAIR>(qp, Cg + (int64_t)qrow * D, Sg + (int64_t)qrow * D, 16 * s + 8 * hh, HALF,
+                                       qb[s], qb[s + NS / 2]);
 #pragma unroll
         for (int s = 0; s < NS; ++s) db[s] = load_chunk<T>(dp + 16 * s + 8 * hh).w;
     }
@@ -613,7 +617,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) dqacc[mb][i] = 0.0f;
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
-    const int pr = pi_row(n), fr = swz_row<D>(pr);
     const int q_hi = min(q0 + 32 * NW, L);
     const int kend = a.causal ? q_hi : L;
     const int n_kt = (kend + KT - 1) / KT;
@@ -636,30 +639,37 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             // ---- S^T and dP^T: lane (n, hh) gets query qi against keys k0 + 32*blk + 16hh + i
-            const int rr = blk * 32 + pr;
+            const int rr = blk * 32 + n;  // pi order: MFMA row n holds key k0 + 32*blk + pi(n)
             f32x16 sacc, dpacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int off = rr * D + 8 * ((2 * s + hh) ^ fr);
+                const int off = rr * PA + 16 * s + 8 * hh;
                 sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&ka[off]), qb[s], sacc);
                 dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&va[off]), db[s], dpacc);
             }
             const int thr = kmax - (k0 + 32 * blk + 16 * hh);  // key ... + i is masked iff i > thr
             u32x4 dsk[2];
+            auto probs = [&](auto masked) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float ds[8];
+                for (int s = 0; s < 2; ++s) {
+                    float ds[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 8 * s + j;
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lse2));
-                    if (i > thr) pv = 0.0f;
-                    ds[j] = pv * (dpacc[i] - del);
+                    for (int j = 0; j < 8; ++j) {
+                        const int i = 8 * s + j;
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lse2));
+                        if (decltype(masked)::value && i > thr) pv = 0.0f;
+                        ds[j] = pv * (dpacc[i] - del);
+                    }
+                    dsk[s] = pack<T>(ds).w;
                 }
-                dsk[s] = pack<T>(ds).w;
-            }
+            };
+            // wave-uniform: the block's last key against the wave's smallest kept bound
+            if (k0 + 32 * blk + 31 > (a.causal ? min(qw0, L - 1) : L - 1))
+                probs(std::true_type{});
+            else
+                probs(std::false_type{});
             // ---- dQ'^T += K'^T dS^T
 #pragma unroll
             for (int mb = 0; mb < D / 32; ++mb)
@@ -667,9 +677,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 for (int s = 0; s < 2; ++s) {
                     const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
                     const int e = mb * 32 + tr_col;
-                    const int sw = 8 * ((e >> 3) ^ swz_tr<D>(tr_row)) + (e & 7);
-                    const i16x4 lo = bwd_tr16(&ktr[r * D + sw]);
-                    const i16x4 hi = bwd_tr16(&ktr[(r + 4) * D + sw]);
+                    const i16x4 lo = bwd_tr16(&ktr[r * PT + e]);
+                    const i16x4 hi = bwd_tr16(&ktr[(r + 4) * PT + e]);
                     dqacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
                                                                                                 6, 7)),
                                              dsk[s], dqacc[mb]);
