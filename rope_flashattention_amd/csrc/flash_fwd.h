@@ -264,6 +264,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     const int kend = a.causal ? q_hi : L;
     const int n_kt = (kend + kBN - 1) / kBN;
     const int wave_kend = a.causal ? min(q0 + 32, L) : L;
+    const int kmax = a.causal ? min(qi, L - 1) : L - 1;  // this lane's last key
 
     u32x4 kx[NKI], ky[NKI], kc[NKI], ks[NKI], kc2[NKI], ks2[NKI], vr[NVI];
     int32_t kpos[NKI];
@@ -395,15 +396,15 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                     sacc[1] = Mfma<T>::run(kv1, qreg[u], sacc[1]);
                 }
             }
-            // ---- masks: causal (key > query) and the ragged end of the sequence
+            // ---- masks: causal (key > query) and the ragged end of the sequence: key
+            // k0 + 32*blk + 16h + i is dropped iff it exceeds this lane's last key kmax
             if ((a.causal && k0 + kBN - 1 > q0) || k0 + kBN > L) {
+                const int thr = kmax - (k0 + 16 * h);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + 32 * blk + 16 * h + i;
-                        if ((a.causal && key > qi) || key >= L) sacc[blk][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (32 * blk + i > thr) sacc[blk][i] = -INFINITY;
             }
             // ---- P = exp2(S - m) rounded to T, and this lane's part of the tile row sum
             auto exp_pack = [&]() {
