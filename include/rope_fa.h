@@ -395,7 +395,10 @@ typedef struct rope_decode_params {
     int32_t max_blocks_per_seq;   /* block-table row length, >= 1 */
     int32_t num_blocks;           /* physical cache blocks, >= 1 */
     int32_t max_seqlen;           /* HOST bound of cache_seqlens, 1..max_blocks_per_seq*block_size */
-    int32_t num_splits;           /* key-range splits per sequence: 0 = the library's choice, else 1..256 */
+    int32_t num_splits;           /* key-range splits per sequence: 0 = the library's choice, else 1..256;
+                                     each split covers the same number of keys, ceil(max_seqlen /
+                                     num_splits) rounded up to 32, so shorter sequences leave their last
+                                     splits empty */
     float softmax_scale;          /* multiplies q.k before the softmax */
     int64_t q_stride[2];          /* {batch, head} in elements; head_dim stride 1 */
     int64_t o_stride[2];

@@ -131,10 +131,18 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
 
     int L = min(a.seqlens[b], a.max_seqlen);
     L = max(L, 0);
-    int chunk = (L + a.nsplit - 1) / a.nsplit;
-    chunk = (chunk + 31) & ~31;
-    const int k_begin = min(split * chunk, L);
-    const int k_end = min(L, k_begin + chunk);
+    // splits of a fixed length (from the host bound): every non-empty split has the same
+    // work, and a shorter sequence simply leaves its last splits empty
+    const int k_begin = min(split * a.chunk, L);
+    const int k_end = min(L, k_begin + a.chunk);
+    if (k_begin >= k_end) {  // empty split (wave-uniform): only (m, l) = (-inf, 0) is written
+        if (hvalid && hh == 0) {
+            const int64_t pi = ((int64_t)b * a.hq + h) * a.nsplit + split;
+            a.ws_m[pi] = kNegInf;
+            a.ws_l[pi] = 0.0f;
+        }
+        return;
+    }
     const int lb0 = k_begin < k_end ? logical_block(a, k_begin) : 0;
     int tabv = 0;
     if (a.table_regs && k_begin < k_end) {
@@ -326,7 +334,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     float o = 0.0f, lsum = 0.0f;
     if (M != -__builtin_inff()) {
         for (int s = 0; s < live; ++s) {
-            const float w = exp2f(a.ws_m[p0 + s] - M);   // empty splits: m = -inf, w = 0
+            const float ms = a.ws_m[p0 + s];
+            if (ms == -__builtin_inff()) continue;  // empty split: its partial O is not written
+            const float w = exp2f(ms - M);
             lsum += w * a.ws_l[p0 + s];
             o += w * a.ws_o[(p0 + s) * D + d];
         }
@@ -342,10 +352,15 @@ int decode_num_splits(const rope_decode_params* p) {
     if (p->num_splits > 0) return p->num_splits;
     const int g = p->hq / p->hkv;
     const int64_t units = (int64_t)p->batch * p->hkv * ((g + 31) / 32);
-    int64_t ns = (2048 + units - 1) / units;                     // about 8 waves per CU
+    // about 8 waves per CU when every sequence is at the bound (splits have a fixed length,
+    // max_seqlen / ns, so shorter sequences leave some of them empty); an odd count makes
+    // consecutive splits of a sequence fall on different XCDs (workgroups are placed round
+    // robin by linear id, split fastest), so the empty high splits are spread evenly
+    int64_t ns = (2048 + units - 1) / units;
     const int64_t by_len = ((int64_t)p->max_seqlen + 127) / 128;  // at least 128 keys per split
     ns = ns < by_len ? ns : by_len;
-    ns = ns < 256 ? ns : 256;
+    if (ns > 1 && (ns & 1) == 0) ns += 1;
+    ns = ns < 255 ? ns : 255;
     return (int)(ns < 1 ? 1 : ns);
 }
 
