@@ -275,8 +275,9 @@ typedef struct rope_attn_bwd_params {
     uint8_t rsv[16];            /* reserved, must be zero */
 } rope_attn_bwd_params;
 
-/* Workspace bytes rope_flash_attn_bwd needs (one float per query row and q head), or 0
- * when the shapes are invalid.  Host only. */
+/* Workspace bytes rope_flash_attn_bwd needs, or 0 when the shapes are invalid: one float
+ * per query row and q head (rowsum(dO * O)), then the rotated rows q' (rows x hq x head_dim)
+ * and k' (rows x hkv x head_dim) in the dtype, each part 256-byte aligned.  Host only. */
 uint64_t rope_flash_attn_bwd_workspace_size(const rope_attn_bwd_params* p);
 
 /*
@@ -292,7 +293,7 @@ uint64_t rope_flash_attn_bwd_workspace_size(const rope_attn_bwd_params* p);
  * Supported: F16/BF16, head_dim 64 or 128, causal or not, dense or varlen, GQA, both
  * pairings.  float32 accumulation; outputs rounded once to dtype.
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, WORKSPACE, HIP.  Three kernel launches
- * (row deltas, dk/dv, dq).
+ * (row deltas with the rotated q', k'; dk/dv; dq).
  */
 rope_status rope_flash_attn_bwd(const rope_attn_bwd_params* p, void* hip_stream);
 

@@ -9,7 +9,9 @@
 // GQA: a kv head's dk and dv sum over the q heads of its group.
 //
 // Three kernels, no atomics:
-//   * bwd_delta_kernel: delta per (query row, q head) into the workspace.
+//   * bwd_prep_kernel: per (query row, q head) delta and the rotated row q' = M q, per
+//     (key row, kv head) k' = M k, into the workspace (so the two main kernels stage plain
+//     copies; only their epilogues use the tables).
 //   * bwd_dkv_kernel: a workgroup of 4 waves owns 128 keys of one (sequence, kv head); each
 //     wave keeps its 32 keys' rotated K' and V as MFMA B operands in registers and
 //     accumulates dV^T and dK'^T over every q head of the group and every query block of
@@ -20,7 +22,7 @@
 //     dO^T and Q'^T.
 //   * bwd_dq_kernel: a workgroup of 8 waves owns 256 query rows of one (sequence, q head);
 //     each wave keeps its 32 rows' Q' and dO as B operands and, per 64-key tile staged in
-//     LDS (K' rotated while staging, V), forms S^T, dP^T and dS^T and accumulates
+//     LDS (K', V), forms S^T, dP^T and dS^T and accumulates
 //     dQ'^T += K'^T dS^T (K'^T by the transposing read).
 // An LDS tile read both ways is stored twice: rows in the pi order for the row reads and
 // in natural order for the transposing reads, each at a padded pitch (bank-conflict free
@@ -46,7 +48,9 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;                // workspace [hq, lse_stride]
+    float* delta;                // workspace [hq, rows]
+    void* qrot;                  // workspace [hq, rows, D]: q' of every query row
+    void* krot;                  // workspace [hkv, rows, D]: k' of every key row
     const int32_t* cu_seqlens;   // nullptr: dense
     int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // {batch, token, head}
     int32_t batch, hq, hkv, group, seqlen, table_seq_rows, lse_stride, causal;
@@ -173,34 +177,62 @@ __device__ __forceinline__ void load_rotated_pair(const T* p, const T* crow, con
     rope_fwd_packed<T, PAIR>(x, y, c0, s0, c1, s1);
 }
 
-// ============================================================================ delta
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-    constexpr int CH = D / 8;  // lanes per (row, head), a power of two
+// ============================================================================ prep
+// Item (row, j) for j < hq: delta of q head j and q'; j >= hq: k' of kv head j - hq.  D/16
+// lanes per item, lane c owning columns 8c..8c+7 and their rotation partners + D/2.
+template <typename T, int D, int PAIR>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int CH = D / 16;  // lanes per item, a power of two
+    constexpr int HALF = D / 2;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t idx = gid / CH;
-    const int c = (int)(gid - idx * CH);
-    const int64_t row = idx / a.hq;
-    const int h = (int)(idx - row * a.hq);
+    const int c = (int)(gid - idx * CH) * 8;
+    const int nh = a.hq + a.hkv;
+    const int64_t row = idx / nh;
+    const int j = (int)(idx - row * nh);
     if (row >= a.rows) return;  // the whole CH-lane group leaves together
-    int64_t oo, od;
-    if (a.cu_seqlens) {
-        oo = row * a.os[1];
-        od = row * a.dos[1];
-    } else {
-        const int64_t b = row / a.seqlen, s = row - b * a.seqlen;
-        oo = b * a.os[0] + s * a.os[1];
-        od = b * a.dos[0] + s * a.dos[1];
+    int64_t b = 0, s = row, tab = row;
+    if (!a.cu_seqlens) {
+        b = row / a.seqlen;
+        s = row - b * a.seqlen;
+        tab = (a.table_seq_rows ? b * a.table_seq_rows : 0) + s;
     }
-    float x[8], y[8];
-    unpack<T>(load_chunk<T>(reinterpret_cast<const T*>(a.o) + oo + (int64_t)h * a.os[2] + c * 8), x);
-    unpack<T>(load_chunk<T>(reinterpret_cast<const T*>(a.dout) + od + (int64_t)h * a.dos[2] + c * 8), y);
-    float sum = 0.0f;
+    const T* crow = PAIR ? reinterpret_cast<const T*>(a.cos) + tab * D : nullptr;
+    const T* srow = PAIR ? reinterpret_cast<const T*>(a.sin) + tab * D : nullptr;
+    u32x4 x, y;
+    if (j < a.hq) {
+        const int64_t tq = a.cu_seqlens ? row * a.qs[1] : b * a.qs[0] + s * a.qs[1];
+        const int64_t to = a.cu_seqlens ? row * a.os[1] : b * a.os[0] + s * a.os[1];
+        const int64_t td = a.cu_seqlens ? row * a.dos[1] : b * a.dos[0] + s * a.dos[1];
+        load_rotated_pair<T, PAIR>(reinterpret_cast<const T*>(a.q) + tq + (int64_t)j * a.qs[2], crow, srow, c, HALF,
+                                   x, y);
+        T* dst = reinterpret_cast<T*>(a.qrot) + ((int64_t)j * a.rows + row) * D + c;
+        *reinterpret_cast<u32x4*>(dst) = x;
+        *reinterpret_cast<u32x4*>(dst + HALF) = y;
+        const T* op = reinterpret_cast<const T*>(a.o) + to + (int64_t)j * a.os[2] + c;
+        const T* dp = reinterpret_cast<const T*>(a.dout) + td + (int64_t)j * a.dos[2] + c;
+        float o0[8], o1[8], d0[8], d1[8];
+        unpack<T>(load_chunk<T>(op), o0);
+        unpack<T>(load_chunk<T>(op + HALF), o1);
+        unpack<T>(load_chunk<T>(dp), d0);
+        unpack<T>(load_chunk<T>(dp + HALF), d1);
+        float sum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sum = __builtin_fmaf(x[e], y[e], sum);
+        for (int e = 0; e < 8; ++e) sum = __builtin_fmaf(o0[e], d0[e], sum);
 #pragma unroll
-    for (int m = CH >> 1; m > 0; m >>= 1) sum += __shfl_xor(sum, m, CH);
-    if (c == 0) a.delta[(int64_t)h * a.lse_stride + row] = sum;
+        for (int e = 0; e < 8; ++e) sum = __builtin_fmaf(o1[e], d1[e], sum);
+#pragma unroll
+        for (int m = CH >> 1; m > 0; m >>= 1) sum += __shfl_xor(sum, m, CH);
+        if (c == 0) a.delta[(int64_t)j * a.rows + row] = sum;
+    } else {
+        const int kh = j - a.hq;
+        const int64_t tk = a.cu_seqlens ? row * a.ks[1] : b * a.ks[0] + s * a.ks[1];
+        load_rotated_pair<T, PAIR>(reinterpret_cast<const T*>(a.k) + tk + (int64_t)kh * a.ks[2], crow, srow, c, HALF,
+                                   x, y);
+        T* dst = reinterpret_cast<T*>(a.krot) + ((int64_t)kh * a.rows + row) * D + c;
+        *reinterpret_cast<u32x4*>(dst) = x;
+        *reinterpret_cast<u32x4*>(dst + HALF) = y;
+    }
 }
 
 // Epilogue helper: scale the 4-value groups of a transposed accumulator (lane holds column
@@ -266,36 +298,18 @@ __device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], floa
 
 // ============================================================================ staging
 // One staging item: the 8-element chunks at columns c and c + D/2 of one row of two
-// tensors (the first is rotated, the second copied) and, when rotating, the row's table
-// chunks (rotate-half: columns c..c+7; interleaved: both).  Loaded one block ahead into
-// registers, rotated and written to LDS at the start of the next block.
+// tensors, loaded one block ahead into registers and written to LDS at the start of the
+// next block.
 struct StageItem {
-    u32x4 a0, a1, b0, b1, c0, s0, c1, s1;
+    u32x4 a0, a1, b0, b1;
 };
 
-template <typename T, int PAIR>
-__device__ __forceinline__ void stage_load(StageItem& s, const T* arow, const T* brow, const T* crow, const T* srow,
-                                           int c, int half) {
+template <typename T>
+__device__ __forceinline__ void stage_load(StageItem& s, const T* arow, const T* brow, int c, int half) {
     s.a0 = load_chunk<T>(arow + c).w;
     s.a1 = load_chunk<T>(arow + c + half).w;
     s.b0 = load_chunk<T>(brow + c).w;
     s.b1 = load_chunk<T>(brow + c + half).w;
-    if (PAIR != 0) {
-        s.c0 = load_chunk<T>(crow + c).w;
-        s.s0 = load_chunk<T>(srow + c).w;
-    }
-    if (PAIR == 2) {
-        s.c1 = load_chunk<T>(crow + c + half).w;
-        s.s1 = load_chunk<T>(srow + c + half).w;
-    }
-}
-
-// The Rope op (M) on a staged item's first tensor.
-template <typename T, int PAIR>
-__device__ __forceinline__ void stage_rotate(const StageItem& s, u32x4& px, u32x4& py) {
-    px = s.a0;
-    py = s.a1;
-    rope_fwd_packed<T, PAIR>(px, py, s.c0, s.s0, s.c1, s.s1);
 }
 
 // Writes chunk pair (c, c + D/2) (element columns) of row r of a 32-row-block tile: x, y
@@ -346,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
     const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
-    const T* Qb = reinterpret_cast<const T*>(a.q) + sq.bq;
+    const T* Qr = reinterpret_cast<const T*>(a.qrot) + sq.tok * D;  // q' rows of this sequence
     const T* Db = reinterpret_cast<const T*>(a.dout) + sq.bdo;
 
     // ---- staging role: item (row sr, chunk pair sc) of each 32-row block; rows past the
@@ -360,19 +374,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     auto load_block = [&](int hi, int q0) {
         const int h = kvh * a.group + hi;
         const int qi = min(q0 + sr, L - 1);
-        stage_load<T, PAIR>(pre, Qb + (int64_t)qi * a.qs[1] + (int64_t)h * a.qs[2],
-                            Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], Cg + (int64_t)qi * D,
-                            Sg + (int64_t)qi * D, sc, HALF);
+        stage_load<T>(pre, Qr + ((int64_t)h * a.rows + qi) * D, Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], sc,
+                      HALF);
         const int64_t idx = (int64_t)h * a.lse_stride + sq.tok + min(q0 + (tid & 31), L - 1);
         pre_l = a.lse[idx];
         pre_d = a.delta[idx];
     };
     auto store_block = [&](int buf, int q0) {
         if (stager) {
-            u32x4 px, py;
-            stage_rotate<T, PAIR>(pre, px, py);
-            store_rowcopy<T, D>(sQa[buf], sr, sc, px, py);
-            store_trcopy<T, D>(sQt[buf], sr, sc, px, py);
+            store_rowcopy<T, D>(sQa[buf], sr, sc, pre.a0, pre.a1);
+            store_trcopy<T, D>(sQt[buf], sr, sc, pre.a0, pre.a1);
             store_rowcopy<T, D>(sDa[buf], sr, sc, pre.b0, pre.b1);
             store_trcopy<T, D>(sDt[buf], sr, sc, pre.b0, pre.b1);
         }
@@ -387,12 +398,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     // ---- this lane's key: rotated K' and V as B operands (column n = key, k = d)
     u32x4 kb[NS], vb[NS];
     {
-        const T* kp = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)key * a.ks[1] + (int64_t)kvh * a.ks[2];
+        const T* kp = reinterpret_cast<const T*>(a.krot) + ((int64_t)kvh * a.rows + sq.tok + key) * D;
         const T* vp = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)key * a.vs[1] + (int64_t)kvh * a.vs[2];
 #pragma unroll
-        for (int s = 0; s < NS / 2; ++s)
-            load_rotated_pair<T, PAIR>(kp, Cg + (int64_t)key * D, Sg + (int64_t)key * D, 16 * s + 8 * hh, HALF, kb[s],
-                                       kb[s + NS / 2]);
+        for (int s = 0; s < NS; ++s) kb[s] = load_chunk<T>(kp + 16 * s + 8 * hh).w;
 #pragma unroll
         for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
         // complete these loads here: otherwise the loop's first use would wait for every
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 
     const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
     const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
-    const T* Kg = reinterpret_cast<const T*>(a.k) + sq.bk + (int64_t)kvh * a.ks[2];
+    const T* Kr = reinterpret_cast<const T*>(a.krot) + ((int64_t)kvh * a.rows + sq.tok) * D;  // k' rows
     const T* Vg = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)kvh * a.vs[2];
 
     // ---- staging: NKI items per thread of each key tile; rows past the end re-read the
@@ -571,8 +580,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
             const int it = (tid + j * NT) % KITEMS;  // spare threads load a duplicate, never stored
             const int r = it / CPR, c = (it % CPR) * 8;
             const int kr = min(k0 + r, L - 1);
-            stage_load<T, PAIR>(pre[j], Kg + (int64_t)kr * a.ks[1], Vg + (int64_t)kr * a.vs[1],
-                                Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, c, HALF);
+            stage_load<T>(pre[j], Kr + (int64_t)kr * D, Vg + (int64_t)kr * a.vs[1], c, HALF);
         }
     };
     auto store_tile = [&](int buf) {
@@ -581,10 +589,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
             const int it = tid + j * NT;
             if (KITEMS % NT == 0 || it < KITEMS) {
                 const int r = it / CPR, c = (it % CPR) * 8;
-                u32x4 px, py;
-                stage_rotate<T, PAIR>(pre[j], px, py);
-                store_rowcopy<T, D>(sKa[buf], r, c, px, py);
-                store_trcopy<T, D>(sKt[buf], r, c, px, py);
+                store_rowcopy<T, D>(sKa[buf], r, c, pre[j].a0, pre[j].a1);
+                store_trcopy<T, D>(sKt[buf], r, c, pre[j].a0, pre[j].a1);
                 store_rowcopy<T, D>(sVa[buf], r, c, pre[j].b0, pre[j].b1);
             }
         }
@@ -593,12 +599,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     // ---- this lane's query row: rotated Q' and dO as B operands (column n = query, k = d)
     u32x4 qb[NS], db[NS];
     {
-        const T* qp = reinterpret_cast<const T*>(a.q) + sq.bq + (int64_t)qrow * a.qs[1] + (int64_t)h * a.qs[2];
+        const T* qp = reinterpret_cast<const T*>(a.qrot) + ((int64_t)h * a.rows + sq.tok + qrow) * D;
         const T* dp = reinterpret_cast<const T*>(a.dout) + sq.bdo + (int64_t)qrow * a.dos[1] + (int64_t)h * a.dos[2];
 #pragma unroll
-        for (int s = 0; s < NS / 2; ++s)
-            load_rotated_pair<T, PAIR>(qp, Cg + (int64_t)qrow * D, Sg + (int64_t)qrow * D, 16 * s + 8 * hh, HALF,
-                                       qb[s], qb[s + NS / 2]);
+        for (int s = 0; s < NS; ++s) qb[s] = load_chunk<T>(qp + 16 * s + 8 * hh).w;
 #pragma unroll
         for (int s = 0; s < NS; ++s) db[s] = load_chunk<T>(dp + 16 * s + 8 * hh).w;
     }
@@ -703,8 +707,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 template <typename T, int D, int PAIR>
 static void launch_bwd_typed(const BwdArgs& a, int maxlen, hipStream_t stream) {
     constexpr int NW = BWD_DQ_NW, KT = BWD_DQ_KT;
-    const int64_t dthreads = (int64_t)a.rows * a.hq * (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream, a);
+    const int64_t pthreads = (int64_t)a.rows * (a.hq + a.hkv) * (D / 16);
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D, PAIR>), dim3((unsigned)((pthreads + 255) / 256)), dim3(256), 0, stream, a);
     BwdArgs g = a;
     g.kv_tiles = (maxlen + 127) / 128;
     g.q_tiles = (maxlen + 32 * NW - 1) / (32 * NW);
@@ -723,10 +727,24 @@ static void launch_bwd_pair(const BwdArgs& a, int pair, int maxlen, hipStream_t 
     }
 }
 
-uint64_t flash_bwd_workspace_bytes(const rope_attn_params* f) {
-    const int64_t rows = f->cu_seqlens ? (int64_t)f->ntokens : (int64_t)f->batch * f->seqlen;
-    return (uint64_t)rows * (uint64_t)f->hq * 4u;
+// Workspace: delta [hq, rows] float32, then q' [hq, rows, D] and k' [hkv, rows, D] of the
+// input dtype, each region starting on a 256-byte boundary.
+struct BwdWorkspace {
+    uint64_t delta, qrot, krot, total;  // byte offsets and size
+};
+static BwdWorkspace bwd_workspace(const rope_attn_params* f) {
+    const uint64_t rows = f->cu_seqlens ? (uint64_t)f->ntokens : (uint64_t)f->batch * (uint64_t)f->seqlen;
+    const uint64_t e = (uint64_t)dtype_bytes(f->dtype);
+    auto up = [](uint64_t x) { return (x + 255u) & ~(uint64_t)255u; };
+    BwdWorkspace w;
+    w.delta = 0;
+    w.qrot = up(rows * (uint64_t)f->hq * 4u);
+    w.krot = w.qrot + up(rows * (uint64_t)f->hq * (uint64_t)f->head_dim * e);
+    w.total = w.krot + up(rows * (uint64_t)f->hkv * (uint64_t)f->head_dim * e);
+    return w;
 }
+
+uint64_t flash_bwd_workspace_bytes(const rope_attn_params* f) { return bwd_workspace(f).total; }
 
 hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream) {
     const rope_attn_params* f = &p->fwd;
@@ -742,7 +760,11 @@ hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream) {
     a.dq = p->dq;
     a.dk = p->dk;
     a.dv = p->dv;
-    a.delta = reinterpret_cast<float*>(p->workspace);
+    const BwdWorkspace ws = bwd_workspace(f);
+    char* wsp = reinterpret_cast<char*>(p->workspace);
+    a.delta = reinterpret_cast<float*>(wsp + ws.delta);
+    a.qrot = wsp + ws.qrot;
+    a.krot = wsp + ws.krot;
     a.cu_seqlens = f->cu_seqlens;
     for (int i = 0; i < 3; ++i) {
         a.qs[i] = f->q_stride[i];

@@ -275,8 +275,11 @@ def valid_bwd_params(**fwd_kw):
 
 def test_bwd_workspace_size(ropelib):
     p = valid_bwd_params()
-    # one float per (query row, q head): B2 x S100 rows, 8 heads
-    assert ropelib.rope_flash_attn_bwd_workspace_size(ctypes.byref(p)) == 2 * 100 * 8 * 4
+    # B2 x S100 rows: delta (one float per row and q head), then q' (8 heads) and k' (2 kv
+    # heads) in the dtype (2 bytes), each region on a 256-byte boundary
+    rows = 2 * 100
+    delta = (rows * 8 * 4 + 255) // 256 * 256
+    assert ropelib.rope_flash_attn_bwd_workspace_size(ctypes.byref(p)) == delta + rows * 8 * 128 * 2 + rows * 2 * 128 * 2
     p.fwd.lse = None
     assert ropelib.rope_flash_attn_bwd_workspace_size(ctypes.byref(p)) == 0
 
