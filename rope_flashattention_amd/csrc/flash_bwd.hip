@@ -178,7 +178,7 @@ __device__ __forceinline__ void load_rotated_pair(const T* p, const T* crow, con
 }
 
 // ============================================================================ prep
-// Item (row, j) for j < hq: delta of q head j and q'; j >= hq: k' of kv head j - hq.  D/16
+// Item (j, row) for j < hq: delta of q head j and q'; j >= hq: k' of kv head j - hq.  D/16
 // lanes per item, lane c owning columns 8c..8c+7 and their rotation partners + D/2.
 template <typename T, int D, int PAIR>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
@@ -187,10 +187,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t idx = gid / CH;
     const int c = (int)(gid - idx * CH) * 8;
-    const int nh = a.hq + a.hkv;
-    const int64_t row = idx / nh;
-    const int j = (int)(idx - row * nh);
-    if (row >= a.rows) return;  // the whole CH-lane group leaves together
+    // head-major items: a wave covers consecutive rows of one head (contiguous in BNSD
+    // inputs and in the workspace)
+    const int j = (int)(idx / a.rows);
+    const int64_t row = idx - (int64_t)j * a.rows;
+    if (j >= a.hq + a.hkv) return;  // the whole CH-lane group leaves together
     int64_t b = 0, s = row, tab = row;
     if (!a.cu_seqlens) {
         b = row / a.seqlen;
