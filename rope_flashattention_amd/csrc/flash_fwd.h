@@ -201,64 +201,6 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     const int32_t* Pg = a.pos + sv.tbase;
     const float* Fg = a.inv_freq + (a.inv_freq_rows > 1 ? (int64_t)b * HALF : 0);
 
-    // ------------------------------------------------------------ Q' in registers
-    // lane holds Q'[qi][16u + 8h + e], u < D/16, e < 8 (the MFMA B-operand layout);
-    // chunk u < D/32 and chunk u + D/32 of the same lane are columns d and d + D/2.
-    vec qreg[D / 16];
-    {
-        const T* qp = reinterpret_cast<const T*>(a.q) + sv.qbase + (int64_t)qi * a.qs[1] + (int64_t)head * a.qs[2];
-#pragma unroll
-        for (int u = 0; u < D / 32; ++u) {
-            const int d = 16 * u + 8 * h;
-            float x[8] = {}, y[8] = {};
-            if (qi < L) {
-                unpack<T>(load_chunk<T>(qp + d), x);
-                unpack<T>(load_chunk<T>(qp + d + HALF), y);
-                if constexpr (ROT == kRotHalfTable) {
-                    float c[8], s[8];
-                    unpack<T>(load_chunk<T>(Cg + (int64_t)qi * D + d), c);
-                    unpack<T>(load_chunk<T>(Sg + (int64_t)qi * D + d), s);
-                    rotate_pair(x, y, c, s, c, s);
-                } else if constexpr (ROT == kRotInterTable) {
-                    float c0[8], s0[8], c1[8], s1[8];
-                    unpack<T>(load_chunk<T>(Cg + (int64_t)qi * D + d), c0);
-                    unpack<T>(load_chunk<T>(Sg + (int64_t)qi * D + d), s0);
-                    unpack<T>(load_chunk<T>(Cg + (int64_t)qi * D + d + HALF), c1);
-                    unpack<T>(load_chunk<T>(Sg + (int64_t)qi * D + d + HALF), s1);
-                    rotate_interleaved(x, c0, s0);
-                    rotate_interleaved(y, c1, s1);
-                } else if constexpr (ROT == kRotHalfGen) {
-                    float f[8], c[8], s[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] = Fg[d + e];
-                    u32x4 cc, ss;
-                    gen_table_chunk<T>(Pg[qi], a.pos_scale, f, cc, ss);
-                    unpack<T>(Chunk8<T>{cc}, c);
-                    unpack<T>(Chunk8<T>{ss}, s);
-                    rotate_pair(x, y, c, s, c, s);
-                } else if constexpr (ROT == kRotInterGen) {
-                    float c0[8], s0[8], c1[8], s1[8];
-                    u32x4 cc, ss;
-                    gen_table_chunk_inter<T>(Pg[qi], a.pos_scale, Fg + d / 2, cc, ss);
-                    unpack<T>(Chunk8<T>{cc}, c0);
-                    unpack<T>(Chunk8<T>{ss}, s0);
-                    gen_table_chunk_inter<T>(Pg[qi], a.pos_scale, Fg + (d + HALF) / 2, cc, ss);
-                    unpack<T>(Chunk8<T>{cc}, c1);
-                    unpack<T>(Chunk8<T>{ss}, s1);
-                    rotate_interleaved(x, c0, s0);
-                    rotate_interleaved(y, c1, s1);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                x[e] *= a.scale_log2;
-                y[e] *= a.scale_log2;
-            }
-            qreg[u] = __builtin_bit_cast(vec, pack<T>(x).w);
-            qreg[u + D / 32] = __builtin_bit_cast(vec, pack<T>(y).w);
-        }
-    }
-
     // ------------------------------------------------------------ tile staging
     const int q_hi = min(qt * QT + QT, L);
     const int kend = a.causal ? q_hi : L;
@@ -359,6 +301,93 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
         }
     };
 
+    // ------------------------------------------------------------ Q' in registers
+    // lane holds Q'[qi][16u + 8h + e], u < D/16, e < 8 (the MFMA B-operand layout);
+    // chunk u < D/32 and chunk u + D/32 of the same lane are columns d and d + D/2.
+    // The raw rows (and their table values) are loaded first, then the first key tile's
+    // loads are issued, and only then is Q rotated: the two memory round trips overlap.
+    // Rows past the end load the last row (finite) and are zeroed after the rotation.
+    constexpr int QU = D / 32;
+    const int qrow = min(qi, L - 1);
+    u32x4 qxr[QU], qyr[QU], qcr[QU], qsr[QU], qc2r[QU], qs2r[QU];
+    float qf[QU][8];
+    int32_t qpos = 0;
+    {
+        const T* qp = reinterpret_cast<const T*>(a.q) + sv.qbase + (int64_t)qrow * a.qs[1] + (int64_t)head * a.qs[2];
+        if constexpr (rot_gen(ROT)) qpos = Pg[qrow];
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            const int d = 16 * u + 8 * h;
+            qxr[u] = load_chunk<T>(qp + d).w;
+            qyr[u] = load_chunk<T>(qp + d + HALF).w;
+            if constexpr (ROT == kRotHalfTable || ROT == kRotInterTable) {
+                qcr[u] = load_chunk<T>(Cg + (int64_t)qrow * D + d).w;
+                qsr[u] = load_chunk<T>(Sg + (int64_t)qrow * D + d).w;
+            }
+            if constexpr (ROT == kRotInterTable) {
+                qc2r[u] = load_chunk<T>(Cg + (int64_t)qrow * D + d + HALF).w;
+                qs2r[u] = load_chunk<T>(Sg + (int64_t)qrow * D + d + HALF).w;
+            }
+            if constexpr (ROT == kRotHalfGen) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[u][e] = Fg[d + e];
+            }
+            if constexpr (ROT == kRotInterGen) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[u][e] = Fg[(e < 4 ? d : d + HALF) / 2 + (e & 3)];
+            }
+        }
+    }
+    vec qreg[D / 16];
+    auto rotate_q = [&]() {
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            float x[8], y[8];
+            unpack<T>(Chunk8<T>{qxr[u]}, x);
+            unpack<T>(Chunk8<T>{qyr[u]}, y);
+            if constexpr (ROT == kRotHalfTable) {
+                float c[8], s[8];
+                unpack<T>(Chunk8<T>{qcr[u]}, c);
+                unpack<T>(Chunk8<T>{qsr[u]}, s);
+                rotate_pair(x, y, c, s, c, s);
+            } else if constexpr (ROT == kRotInterTable) {
+                float c0[8], s0[8], c1[8], s1[8];
+                unpack<T>(Chunk8<T>{qcr[u]}, c0);
+                unpack<T>(Chunk8<T>{qsr[u]}, s0);
+                unpack<T>(Chunk8<T>{qc2r[u]}, c1);
+                unpack<T>(Chunk8<T>{qs2r[u]}, s1);
+                rotate_interleaved(x, c0, s0);
+                rotate_interleaved(y, c1, s1);
+            } else if constexpr (ROT == kRotHalfGen) {
+                float c[8], s[8];
+                u32x4 cc, ss;
+                gen_table_chunk<T>(qpos, a.pos_scale, qf[u], cc, ss);
+                unpack<T>(Chunk8<T>{cc}, c);
+                unpack<T>(Chunk8<T>{ss}, s);
+                rotate_pair(x, y, c, s, c, s);
+            } else if constexpr (ROT == kRotInterGen) {
+                float c0[8], s0[8], c1[8], s1[8];
+                u32x4 cc, ss;
+                gen_table_chunk_inter<T>(qpos, a.pos_scale, &qf[u][0], cc, ss);
+                unpack<T>(Chunk8<T>{cc}, c0);
+                unpack<T>(Chunk8<T>{ss}, s0);
+                gen_table_chunk_inter<T>(qpos, a.pos_scale, &qf[u][4], cc, ss);
+                unpack<T>(Chunk8<T>{cc}, c1);
+                unpack<T>(Chunk8<T>{ss}, s1);
+                rotate_interleaved(x, c0, s0);
+                rotate_interleaved(y, c1, s1);
+            }
+            const float sc = qi < L ? a.scale_log2 : 0.0f;  // rows past the end: zero
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] *= sc;
+                y[e] *= sc;
+            }
+            qreg[u] = __builtin_bit_cast(vec, pack<T>(x).w);
+            qreg[u + D / 32] = __builtin_bit_cast(vec, pack<T>(y).w);
+        }
+    };
+
     // ------------------------------------------------------------ main loop
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -371,9 +400,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
 
     stage_load(0);
+    rotate_q();
     stage_store(0);
-    __syncthreads();
     if (n_kt > 1) stage_load(1);
+    __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
