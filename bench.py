@@ -118,7 +118,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU reaches its steady clocks only after ~100 ms of sustained work: 500 untimed
+    # steps of the benchmarked workload (about 0.1 s) before the K timed ones
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: the S=2048 MHA workload)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
