@@ -10,7 +10,12 @@
 // kernels are bound by HBM bandwidth.
 //
 // Partial kernel (decode_partial_kernel): one wavefront per (sequence, kv head, group of
-// up to 32 q heads, key split).  Per 32-key tile:
+// up to 32 q heads, key split).  Splits have a fixed length, so sequence b has
+// ceil(L_b / chunk) non-empty ones; for batches up to kCompactMaxBatch the grid is a list of
+// only those items (every wave reads the lengths and finds its item by a prefix sum), so
+// every workgroup has the same work up to the last split of a sequence and the
+// dispatcher spreads them evenly over the CUs; larger batches use one workgroup per
+// (split, unit, sequence) and empty splits exit at once.  Per 32-key tile:
 //   * K and V rows arrive by coalesced 16-byte loads (whole 256-byte rows per 16 lanes;
 //     every load of a tile issued back to back, the next tile's loads issued as soon as
 //     this tile is in LDS) and are stored row-major in a wave-private LDS tile whose
@@ -58,6 +63,7 @@ struct DecodeArgs {
     int32_t chunk;      // keys per split (multiple of 32)
     int32_t bs_shift;   // log2(block_size) when it is a power of two, else -1
     int32_t table_regs; // 1: a split's block-table entries fit one register per lane
+    int32_t compact;    // 1: workgroup i takes the i-th non-empty (sequence, unit, split) item
 };
 
 template <typename T> struct DMma;
@@ -107,6 +113,14 @@ __device__ __forceinline__ int physical_block(const DecodeArgs& a, int b, int lb
     return min(max(pb, 0), a.num_blocks - 1);
 }
 
+// Sequences up to which the partial kernel's grid lists only non-empty items.
+constexpr int kCompactMaxBatch = 1024;
+
+// cached length of sequence b as the kernels use it: clamped to [0, max_seqlen]
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+    return max(min(a.seqlens[b], a.max_seqlen), 0);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
     constexpr int NS = D / 16;        // MFMA k-steps over the head dimension
@@ -121,28 +135,55 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
     const int l = threadIdx.x;
     const int n = l & 31;
     const int hh = l >> 5;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / a.ngroups;
-    const int grp = blockIdx.y - kvh * a.ngroups;
-    const int b = blockIdx.z;
+    int split, unit, b;
+    if (a.compact) {
+        // items in the order (sequence, unit, split), non-empty splits only: sequence b owns
+        // units * ceil(L_b / chunk) of them; a wave-wide prefix sum over the lengths, 64
+        // sequences at a time, finds the one that holds item blockIdx.x
+        const int units = a.hkv * a.ngroups;
+        const int item = blockIdx.x;
+        int base = 0;
+        b = -1;
+        int local = 0, nb = 1;
+        for (int b0 = 0; b0 < a.batch; b0 += 64) {
+            const int bi = b0 + l;
+            const int cnt = bi < a.batch ? (seq_len(a, bi) + a.chunk - 1) / a.chunk * units : 0;
+            int inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(inc, o);
+                inc += l >= o ? t : 0;
+            }
+            const int tot = __shfl(inc, 63);
+            if (item < base + tot) {
+                const int lane = __builtin_ctzll(__builtin_amdgcn_ballot_w64(base + inc > item));
+                b = b0 + lane;
+                local = __builtin_amdgcn_readfirstlane(item - base - __shfl(inc - cnt, lane));
+                nb = __builtin_amdgcn_readfirstlane(__shfl(cnt, lane)) / units;
+                break;
+            }
+            base += tot;
+        }
+        if (b < 0) return;  // past the last item
+        unit = local / nb;
+        split = local - unit * nb;
+    } else {
+        split = blockIdx.x;
+        unit = blockIdx.y;
+        b = blockIdx.z;
+    }
+    const int kvh = unit / a.ngroups;
+    const int grp = unit - kvh * a.ngroups;
     const int hin = grp * 32 + n;
     const bool hvalid = hin < a.g;
     const int h = kvh * a.g + (hvalid ? hin : 0);
 
-    int L = min(a.seqlens[b], a.max_seqlen);
-    L = max(L, 0);
+    const int L = seq_len(a, b);
     // splits of a fixed length (from the host bound): every non-empty split has the same
-    // work, and a shorter sequence simply leaves its last splits empty
+    // work up to a sequence's last one; the combine reads only splits below ceil(L / chunk)
     const int k_begin = min(split * a.chunk, L);
     const int k_end = min(L, k_begin + a.chunk);
-    if (k_begin >= k_end) {  // empty split (wave-uniform): only (m, l) = (-inf, 0) is written
-        if (hvalid && hh == 0) {
-            const int64_t pi = ((int64_t)b * a.hq + h) * a.nsplit + split;
-            a.ws_m[pi] = kNegInf;
-            a.ws_l[pi] = 0.0f;
-        }
-        return;
-    }
+    if (k_begin >= k_end) return;  // empty split (wave-uniform)
     const int lb0 = k_begin < k_end ? logical_block(a, k_begin) : 0;
     int tabv = 0;
     if (a.table_regs && k_begin < k_end) {
@@ -323,29 +364,45 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    // one workgroup of D threads per (sequence, q head); thread d owns output column d.
+    // The split statistics are read 64 at a time, one split per lane (each wave computes
+    // them redundantly), and the weighted sum over the splits issues its loads back to back.
+    constexpr float kNegInf = -__builtin_inff();
     const int bh = blockIdx.x;
     const int b = bh / a.hq;
     const int h = bh - b * a.hq;
     const int d = threadIdx.x;
+    const int lane = d & 63;
     const int64_t p0 = (int64_t)bh * a.nsplit;
-    const int live = a.nsplit;
-    float M = -__builtin_inff();
-    for (int s = 0; s < live; ++s) M = fmaxf(M, a.ws_m[p0 + s]);
+    const int live = (seq_len(a, b) + a.chunk - 1) / a.chunk;  // the splits the partial kernel wrote
+    float M = kNegInf;
+    for (int s0 = 0; s0 < live; s0 += 64) M = fmaxf(M, s0 + lane < live ? a.ws_m[p0 + s0 + lane] : kNegInf);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float o = 0.0f, lsum = 0.0f;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < live; ++s) {
-            const float ms = a.ws_m[p0 + s];
-            if (ms == -__builtin_inff()) continue;  // empty split: its partial O is not written
-            const float w = exp2f(ms - M);
-            lsum += w * a.ws_l[p0 + s];
-            o += w * a.ws_o[(p0 + s) * D + d];
+    for (int s0 = 0; s0 < live; s0 += 64) {
+        const int s = s0 + lane;
+        const float w = s < live ? exp2f(a.ws_m[p0 + s] - M) : 0.0f;
+        lsum += s < live ? w * a.ws_l[p0 + s] : 0.0f;
+        const int n = min(64, live - s0);
+        const float* wo = a.ws_o + (p0 + s0) * D + d;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = wo[(int64_t)min(j0 + u, n - 1) * D];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(j0 + u, 63)));
+                o += j0 + u < n ? wj * v[u] : 0.0f;
+            }
         }
-        o = o / lsum;
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+    if (live > 0) o = o / lsum;
     T* orow = reinterpret_cast<T*>(a.out) + (int64_t)b * a.os[0] + (int64_t)h * a.os[1];
     orow[d] = (T)o;
-    if (a.lse && d == 0)
-        a.lse[bh] = M == -__builtin_inff() ? -__builtin_inff() : (M + log2f(lsum)) * 0.69314718055994531f;
+    if (a.lse && d == 0) a.lse[bh] = live > 0 ? (M + log2f(lsum)) * 0.69314718055994531f : kNegInf;
 }
 
 int decode_num_splits(const rope_decode_params* p) {
@@ -353,9 +410,11 @@ int decode_num_splits(const rope_decode_params* p) {
     const int g = p->hq / p->hkv;
     const int64_t units = (int64_t)p->batch * p->hkv * ((g + 31) / 32);
     // about 8 waves per CU when every sequence is at the bound (splits have a fixed length,
-    // max_seqlen / ns, so shorter sequences leave some of them empty); an odd count makes
-    // consecutive splits of a sequence fall on different XCDs (workgroups are placed round
-    // robin by linear id, split fastest), so the empty high splits are spread evenly
+    // max_seqlen / ns, so shorter sequences leave some of them empty; measured on 32
+    // sequences of 1024..8192 keys: 9 splits 4.77 TB/s, 13: 4.46, 17: 4.39, 33: 4.47).  In the
+    // grid of all (split, unit, sequence) triples used above kCompactMaxBatch sequences an
+    // odd count makes consecutive splits of a sequence fall on different XCDs (workgroups
+    // are placed round robin by linear id, split fastest), so empty high splits spread evenly
     int64_t ns = (2048 + units - 1) / units;
     const int64_t by_len = ((int64_t)p->max_seqlen + 127) / 128;  // at least 128 keys per split
     ns = ns < by_len ? ns : by_len;
@@ -371,8 +430,9 @@ uint64_t decode_workspace_bytes(const rope_decode_params* p, int nsplit) {
 
 template <typename T, int D>
 static void launch_typed(const DecodeArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3(a.nsplit, a.hkv * a.ngroups, a.batch), dim3(64), 0, stream,
-                       a);
+    const dim3 grid = a.compact ? dim3((unsigned)a.nsplit * a.hkv * a.ngroups * a.batch)
+                                : dim3(a.nsplit, a.hkv * a.ngroups, a.batch);
+    hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(64), 0, stream, a);
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.batch * a.hq), dim3(D), 0, stream, a);
 }
 
@@ -419,6 +479,7 @@ hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream) {
         if ((1 << sh) == p->block_size) a.bs_shift = sh;
     // blocks one split can touch: chunk / block_size + 1 (an unaligned start)
     a.table_regs = (a.chunk / p->block_size + 2) <= 64;
+    a.compact = p->batch <= kCompactMaxBatch;
     const int key = (p->dtype == ROPE_DT_BF16 ? 0 : 2) + (p->head_dim == 128 ? 1 : 0);
     switch (key) {
         case 0: launch_typed<__bf16, 64>(a, stream); break;

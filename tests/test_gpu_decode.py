@@ -227,3 +227,16 @@ def test_decode_matches_prefill_last_row():
     err = (od[0].float() - o[0, :, S - 1].float()).abs().max().item()
     say(f"decode vs prefill last row: max-abs {err:.3e}")
     assert err <= ATTN_TOL[w.dtype]
+
+
+@pytest.mark.parametrize("batch", [200, 1030])
+def test_decode_many_sequences(batch):
+    # 200 sequences: the partial kernel's list of non-empty (sequence, unit, split) items is
+    # found by a prefix sum over four blocks of 64 lengths; 1030 (above 1024) takes the grid of
+    # all (split, unit, sequence) triples.  Some lengths are zero or clamped.
+    w = small(batch=batch, hq=4, hkv=2, head_dim=64, ctx_range=(0, 90), max_len=96, seed=3500 + batch)
+    ci = wl.generate_cache(w)
+    lens = (ci.ctx + 1).astype(np.int32)
+    lens[::7] = 0
+    lens[3::11] = 96 + 5
+    run_decode(ci, lens=lens, max_seqlen=96, num_splits=3, label=f"{batch} sequences")
