@@ -5,10 +5,10 @@
 // freq along the last axis (cat(freq, freq)); the outputs are sin(emb) and cos(emb).
 // Linear position scaling ([RoPE-fusion blog], section 5.3) divides positions first.
 //
-// One thread owns one token and 8 consecutive frequencies i .. i+7: it computes 8
-// sin/cos pairs once and stores each result twice (columns i and i + D/2 for the
-// rotate-half layout, 2i and 2i + 1 for the interleaved one), so every transcendental
-// evaluation feeds four stores.  The kernel is bound by HBM writes
+// One thread evaluates 8 sin/cos pairs and stores each result twice (columns i and
+// i + D/2 for the rotate-half layout, 2i and 2i + 1 for the interleaved one); the
+// frequencies it takes are chosen so that every store instruction of a wavefront writes
+// one contiguous run (see the kernel).  The kernel is bound by HBM writes
 // (2 * ntokens * D * sizeof(out)).  The exact-angle mode forms angles and sin/cos in
 // float64 and rounds each value once to the output type.
 #include "common.h"
@@ -36,61 +36,95 @@ __device__ __forceinline__ float round_to_odd_f32(double d) {
     return __uint_as_float(u);
 }
 
+// 16 bytes of output values (8 16-bit or 4 float32 elements)
+template <typename TO>
+__device__ __forceinline__ u32x4 piece_bits(const float (&v)[16 / sizeof(TO)]) {
+    if constexpr (sizeof(TO) == 4) {
+        return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    } else {
+        return pack<TO>(v).w;
+    }
+}
+
 template <typename TO, int PAIR, bool EXACT>
 __global__ __launch_bounds__(256) void rope_tables_kernel(TablesArgs a) {
+    // A piece is 16 bytes of one table row: E elements holding FPP frequencies (rotate-half:
+    // columns c..c+E-1 of the first half, stored again at c + D/2; interleaved: columns
+    // c..c+E-1 = frequencies c/2 .. c/2 + E/2 - 1, each twice).  A thread evaluates 8
+    // frequencies, i.e. P pieces; the k-th piece of every lane of a wave is consecutive in
+    // memory (pieces wave_base + 64k + lane), so each store instruction writes 1 KB in one run.
+    constexpr int E = 16 / sizeof(TO);
+    constexpr int FPP = PAIR == ROPE_PAIR_HALF ? E : E / 2;
+    constexpr int P = 8 / FPP;
     const int half = a.head_size >> 1;
-    const int chunks = half >> 3;  // 8-frequency chunks per row
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)a.ntokens * chunks) return;
-    const int t = (int)(gid / chunks);
-    const int j = (int)(gid - (int64_t)t * chunks) * 8;
-    int b = 0;
+    const uint32_t npr = (uint32_t)(PAIR == ROPE_PAIR_HALF ? half : a.head_size) / E;  // pieces per row
+    const uint32_t total = (uint32_t)a.ntokens * npr;
+    const uint32_t wbase = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64u * P);
+    const uint32_t lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 1; i < ROPE_MAX_BATCH; ++i) b += (i < a.batch && t >= a.starts[i]) ? 1 : 0;
-    const float* f = a.inv_freq + (int64_t)b * half + j;
-    const f32x4 f0 = *reinterpret_cast<const f32x4*>(f);
-    const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + 4);
-    float sv[8], cv[8];
-    if (EXACT) {
-        const double p = (double)a.pos[t] / (double)a.pos_scale;
+    for (int k = 0; k < P; ++k) {
+        const uint32_t g = wbase + 64u * k + lane;
+        if (g >= total) break;
+        const int t = (int)(g / npr);
+        const int col = (int)(g - (uint32_t)t * npr) * E;  // first column of the piece
+        const int fi = PAIR == ROPE_PAIR_HALF ? col : col / 2;  // its first frequency
+        int b = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            double sd, cd;
-            sincos(p * (double)(e < 4 ? f0[e] : f1[e - 4]), &sd, &cd);
-            if (sizeof(TO) == 4) {
-                sv[e] = (float)sd;
-                cv[e] = (float)cd;
-            } else {
-                sv[e] = round_to_odd_f32(sd);
-                cv[e] = round_to_odd_f32(cd);
+        for (int i = 1; i < ROPE_MAX_BATCH; ++i) b += (i < a.batch && t >= a.starts[i]) ? 1 : 0;
+        const float* f = a.inv_freq + (int64_t)b * half + fi;
+        float fr[FPP];
+        if constexpr (FPP == 8) {
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(f);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fr[e] = f0[e];
+                fr[e + 4] = f1[e];
             }
+        } else if constexpr (FPP == 4) {
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fr[e] = f0[e];
+        } else {
+            const f32x2 f0 = *reinterpret_cast<const f32x2*>(f);
+            fr[0] = f0[0];
+            fr[1] = f0[1];
         }
-    } else {
+        float sv[FPP], cv[FPP];
+        if (EXACT) {
+            const double p = (double)a.pos[t] / (double)a.pos_scale;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rope_sincos(table_angle(a.pos[t], a.pos_scale, e < 4 ? f0[e] : f1[e - 4]), sv[e], cv[e]);
-    }
-    TO* so = reinterpret_cast<TO*>(a.sin_out) + (int64_t)t * a.head_size;
-    TO* co = reinterpret_cast<TO*>(a.cos_out) + (int64_t)t * a.head_size;
-    if (PAIR == ROPE_PAIR_HALF) {
-        // frequency i fills columns i and i + D/2
-        const Chunk8<TO> sc = pack<TO>(sv);
-        const Chunk8<TO> cc = pack<TO>(cv);
-        store_chunk<TO>(so + j, sc);
-        store_chunk<TO>(so + j + half, sc);
-        store_chunk<TO>(co + j, cc);
-        store_chunk<TO>(co + j + half, cc);
-    } else {
-        // frequency i fills columns 2i and 2i + 1
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-            float s2[8], c2[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                s2[e] = sv[4 * hlf + e / 2];
-                c2[e] = cv[4 * hlf + e / 2];
+            for (int e = 0; e < FPP; ++e) {
+                double sd, cd;
+                sincos(p * (double)fr[e], &sd, &cd);
+                if (sizeof(TO) == 4) {
+                    sv[e] = (float)sd;
+                    cv[e] = (float)cd;
+                } else {
+                    sv[e] = round_to_odd_f32(sd);
+                    cv[e] = round_to_odd_f32(cd);
+                }
             }
-            store_chunk<TO>(so + 2 * j + 8 * hlf, pack<TO>(s2));
-            store_chunk<TO>(co + 2 * j + 8 * hlf, pack<TO>(c2));
+        } else {
+            const int32_t pos = a.pos[t];
+#pragma unroll
+            for (int e = 0; e < FPP; ++e) rope_sincos(table_angle(pos, a.pos_scale, fr[e]), sv[e], cv[e]);
+        }
+        float se[E], ce[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            se[e] = sv[PAIR == ROPE_PAIR_HALF ? e : e / 2];
+            ce[e] = cv[PAIR == ROPE_PAIR_HALF ? e : e / 2];
+        }
+        const u32x4 sb = piece_bits<TO>(se);
+        const u32x4 cb = piece_bits<TO>(ce);
+        TO* so = reinterpret_cast<TO*>(a.sin_out) + (int64_t)t * a.head_size + col;
+        TO* co = reinterpret_cast<TO*>(a.cos_out) + (int64_t)t * a.head_size + col;
+        *reinterpret_cast<u32x4*>(so) = sb;
+        *reinterpret_cast<u32x4*>(co) = cb;
+        if (PAIR == ROPE_PAIR_HALF) {
+            *reinterpret_cast<u32x4*>(so + half) = sb;
+            *reinterpret_cast<u32x4*>(co + half) = cb;
         }
     }
 }
@@ -120,6 +154,7 @@ hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const i
     a.pos_scale = pos_scale;
     a.starts[0] = 0;
     for (int i = 0; i < ROPE_MAX_BATCH; ++i) a.starts[i + 1] = a.starts[i] + (i < batch ? seq_lens[i] : 0);
+    // 8 frequencies per thread: head_size / 16 threads per row
     const int64_t threads = (int64_t)ntokens * (head_size / 16);
     const dim3 grid((unsigned)((threads + 255) / 256));
     switch (out_dtype) {
