@@ -221,13 +221,28 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 kf[j][e] = ROT == kRotHalfGen ? Fg[c + e] : Fg[(e < 4 ? c : c + HALF) / 2 + (e & 3)];
         }
     }
+    // Byte offsets of this thread's staged chunks within a full tile (32-bit, non-negative),
+    // so that each load is a uniform tile base plus one per-lane register offset.
+    uint32_t kob[NKI], tob[NKI], vob[NVI];
+#pragma unroll
+    for (int j = 0; j < NKI; ++j) {
+        const int it = tid + j * NT;
+        const int kap = it / KCH, c = (it % KCH) * 8;
+        kob[j] = (uint32_t)(kap * a.ks[1] + c) * (uint32_t)sizeof(T);
+        tob[j] = (uint32_t)(kap * D + c) * (uint32_t)sizeof(T);
+    }
+#pragma unroll
+    for (int j = 0; j < NVI; ++j) {
+        const int it = tid + j * NT;
+        vob[j] = (uint32_t)((it / (D / 8)) * a.vs[1] + (it % (D / 8)) * 8) * (uint32_t)sizeof(T);
+    }
     auto stage_load = [&](int kt) {
         const int k0 = kt * kBN;
         const bool full = k0 + kBN <= L;
-        const T* kg = Kg + (int64_t)k0 * a.ks[1];
-        const T* vg = Vg + (int64_t)k0 * a.vs[1];
-        const T* cg = Cg + (int64_t)k0 * D;
-        const T* sg = Sg + (int64_t)k0 * D;
+        const char* kg = reinterpret_cast<const char*>(Kg + (int64_t)k0 * a.ks[1]);
+        const char* vg = reinterpret_cast<const char*>(Vg + (int64_t)k0 * a.vs[1]);
+        const char* cg = reinterpret_cast<const char*>(Cg + (int64_t)k0 * D);
+        const char* sg = reinterpret_cast<const char*>(Sg + (int64_t)k0 * D);
         // rows past the end of the sequence re-read its last row: finite data whose scores
         // the mask removes (their P is exactly 0), so no zero fill is needed
 #pragma unroll
@@ -235,16 +250,17 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             const int it = tid + j * NT;
             if (KITEMS % NT == 0 || it < KITEMS) {
                 const int kap = full ? it / KCH : min(it / KCH, L - 1 - k0), c = (it % KCH) * 8;
-                const T* kp = kg + (int64_t)kap * a.ks[1] + c;
-                kx[j] = *reinterpret_cast<const u32x4*>(kp);
-                ky[j] = *reinterpret_cast<const u32x4*>(kp + HALF);
+                const uint32_t ko = full ? kob[j] : (uint32_t)(kap * a.ks[1] + c) * (uint32_t)sizeof(T);
+                const uint32_t to = full ? tob[j] : (uint32_t)(kap * D + c) * (uint32_t)sizeof(T);
+                kx[j] = *reinterpret_cast<const u32x4*>(kg + ko);
+                ky[j] = *reinterpret_cast<const u32x4*>(kg + ko + HALF * sizeof(T));
                 if constexpr (ROT == kRotHalfTable || ROT == kRotInterTable) {
-                    kc[j] = *reinterpret_cast<const u32x4*>(cg + kap * D + c);
-                    ks[j] = *reinterpret_cast<const u32x4*>(sg + kap * D + c);
+                    kc[j] = *reinterpret_cast<const u32x4*>(cg + to);
+                    ks[j] = *reinterpret_cast<const u32x4*>(sg + to);
                 }
                 if constexpr (ROT == kRotInterTable) {
-                    kc2[j] = *reinterpret_cast<const u32x4*>(cg + kap * D + c + HALF);
-                    ks2[j] = *reinterpret_cast<const u32x4*>(sg + kap * D + c + HALF);
+                    kc2[j] = *reinterpret_cast<const u32x4*>(cg + to + HALF * sizeof(T));
+                    ks2[j] = *reinterpret_cast<const u32x4*>(sg + to + HALF * sizeof(T));
                 }
                 if constexpr (rot_gen(ROT)) kpos[j] = Pg[k0 + kap];
             }
@@ -254,7 +270,8 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             const int it = tid + j * NT;
             if (VITEMS % NT == 0 || it < VITEMS) {
                 const int kap = full ? it / (D / 8) : min(it / (D / 8), L - 1 - k0), c = (it % (D / 8)) * 8;
-                vr[j] = *reinterpret_cast<const u32x4*>(vg + (int64_t)kap * a.vs[1] + c);
+                const uint32_t vo = full ? vob[j] : (uint32_t)(kap * a.vs[1] + c) * (uint32_t)sizeof(T);
+                vr[j] = *reinterpret_cast<const u32x4*>(vg + vo);
             }
         }
     };
