@@ -43,6 +43,25 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def gpu_max_clock_mhz():
+    """The GPU agent's maximum engine clock as rocminfo reports it (MHz), or None."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in txt.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        for ln in agent.splitlines():
+            if "Max Clock Freq" in ln:
+                try:
+                    return int(ln.split(":")[1].split()[0])
+                except (IndexError, ValueError):
+                    return None
+    return None
+
+
 def read_traffic(workload_key):
     """HBM bytes per launch from the committed counter summary, if it matches the source."""
     path = os.path.join(ROOT, "profiles", f"traffic_flash_fwd_{workload_key}.txt")
@@ -231,6 +250,13 @@ def main():
         "components": {"rope_tables_ms": round(tab_ms, 5), "attention_ms": round(att_ms, 4),
                        "attention_tflops": round(achieved, 2)},
     }
+    # the dense peak at the clock the agent reports: 256 CUs x 4096 bf16/fp16 FLOP per clock
+    mhz = gpu_max_clock_mhz()
+    if mhz and w.dtype in ("bf16", "f16"):
+        pk = 256 * 4096 * mhz * 1e6 / 1e12
+        result["components"]["max_clock_mhz"] = mhz
+        result["components"]["peak_at_max_clock_tflops"] = round(pk, 1)
+        result["components"]["frac_of_peak_at_max_clock"] = round(achieved / pk, 4)
 
     if not args.no_extras:
         comp = result["components"]
