@@ -87,14 +87,17 @@ def median(xs):
 
 
 def time_events(fn, reps, torch):
-    """Median device time (ms) of fn over reps launches, HIP events on the current stream."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record()
+    """Device time (ms) per call of fn: reps back-to-back calls between two HIP events on the
+    current stream (an event pair around every call adds a few microseconds of queue work,
+    a sizeable share for the HBM-bound kernels of 40-150 us)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    return median([a.elapsed_time(b) for a, b in evs])
+    return a.elapsed_time(b) / reps
 
 
 def cpu_baseline(inp, budget_s):
