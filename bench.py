@@ -340,19 +340,26 @@ def main():
         tpos = torch.arange(16000, dtype=torch.int32, device=dev).repeat(16)
         for Dt in (2048, 512):
             tf = torch.from_numpy(rfa.inv_freq(1e4, Dt, lens, 4096)).to(dev)
+            variants = []
             for dt_name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
                 ts = torch.empty((256000, Dt), dtype=dt, device=dev)
                 tc = torch.empty((256000, Dt), dtype=dt, device=dev)
-                fn = lambda: rfa.rope_tables(tpos, tf, lens, Dt, 1.0, dt, ts, tc)
-                # 30 untimed calls (3-10 ms of writes): after the matrix-bound runs above,
-                # 3 calls left the first timed variant up to 15% slow
-                for _ in range(30):
-                    fn()
-                ms = time_events(fn, 20, torch)
-                tb = 2 * 256000 * Dt * 2 + 4 * 256000 + 4 * 16 * (Dt // 2)
-                comp[f"rope_tables_{dt_name}_T256000_D{Dt}_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
-                comp[f"rope_tables_{dt_name}_T256000_D{Dt}_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-                del ts, tc
+                variants.append((dt_name, (lambda ts=ts, tc=tc, dt=dt: rfa.rope_tables(tpos, tf, lens, Dt, 1.0, dt, ts,
+                                                                                      tc))))
+            # the dtypes are timed in turn, three times each, and the median taken: the first
+            # variant timed after the matrix-bound runs above otherwise reads up to 15% slow
+            times = {name: [] for name, _ in variants}
+            for _ in range(3):
+                for name, fn in variants:
+                    for _ in range(10):
+                        fn()
+                    times[name].append(time_events(fn, 20, torch))
+            tb = 2 * 256000 * Dt * 2 + 4 * 256000 + 4 * 16 * (Dt // 2)
+            for name, _ in variants:
+                ms = median(times[name])
+                comp[f"rope_tables_{name}_T256000_D{Dt}_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
+                comp[f"rope_tables_{name}_T256000_D{Dt}_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del variants
         torch.cuda.empty_cache()
         # fused RMSNorm + RoPE + KV-cache write on a 16 x 4096-token prefill into a paged cache:
         # reads K, V and the table rows, writes K', V into the cache (slots, gamma are small)
