@@ -66,6 +66,26 @@ def test_tables_parity_page_limits(D, dtype):
     assert es.max() <= 2.0 and ec.max() <= 2.0
 
 
+@pytest.mark.parametrize("D", [32, 96, 160])
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_tables_piece_mapping_odd_sizes(D, pairing):
+    """Every dtype and pairing at head sizes whose rows hold an odd number of 16-byte pieces
+    and token counts that end inside a wavefront's run of pieces: all elements, 2 ulp."""
+    dev = device()
+    for T in (1, 5, 37, 301):
+        lens = np.array([T], dtype=np.int32) if T < 37 else np.array([T - 20, 20], dtype=np.int32)
+        pos = np.concatenate([np.arange(L, dtype=np.int32) * 7 for L in lens])
+        f = rfa.inv_freq(1e4, D, lens)
+        for dtype, dn in ((torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32")):
+            s, c = rfa.rope_tables(torch.from_numpy(pos).to(dev), torch.from_numpy(f).to(dev), lens, D, 1.0, dtype,
+                                   pairing=pairing)
+            rs, rc = orc.rope_tables(pos, f, lens, 1.0, "fp32", pairing)
+            es = ulp_err(s.to(torch.float64).cpu().numpy(), rs, dn).max()
+            ec = ulp_err(c.to(torch.float64).cpu().numpy(), rc, dn).max()
+            assert es <= 2.0 and ec <= 2.0, (T, dn, es, ec)
+    say(f"tables D={D} {pairing}: T in (1, 5, 37, 301), f16/bf16/f32 within 2 ulp")
+
+
 def test_tables_segment_index_probe():
     """Exact angles with a different frequency per sequence: recover b(t) from every row."""
     dev = device()
