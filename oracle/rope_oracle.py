@@ -29,8 +29,10 @@ angles formed in float32 (int32 positions, float32 inverse frequencies);
 contiguous GQA grouping (kv head = q head // group); softmax scale passed in.
 
 Parity status: every function below is pinned by tests/test_oracle.py except
-``ntk_base``, whose formula is not on the pages (parity unpinned; only its
-"no change at or below the trained length" property is pinned).
+``ntk_base``, whose formula is not on the pages (parity unpinned against the pages;
+pinned are the page's "no change at or below the trained length" and the reading's
+defining property: the lowest inverse frequency divided by exactly L / L_train, the
+highest unchanged).
 """
 
 from __future__ import annotations

@@ -58,6 +58,23 @@ def test_ntk_base_properties():
     assert np.all(f[1] <= f[0]) and np.all(f[1] > 0) and np.all(f <= 1)
 
 
+def test_ntk_base_reading_stretches_longest_wavelength_by_length_ratio():
+    # The enlargement law is a reading (the page lost it), so this pins the reading's defining
+    # property, not the page: NTK-aware scaling divides the lowest inverse frequency by exactly
+    # the length ratio L / L_train (the longest wavelength then spans the longer context) and
+    # leaves the highest (i = 0, f = 1) unchanged.  A wrong exponent ((D-2)/D for D/(D-2), or
+    # D/2 for D) moves the lowest frequency by a different factor and fails.
+    for D in (64, 128, 256):
+        f0 = orc.inv_freq(1e4, D).astype(np.float64)
+        for L, Lt in ((8192, 4096), (10000, 4096), (32768, 2048), (4097, 4096)):
+            f = orc.inv_freq(orc.ntk_base(1e4, L, Lt, D), D).astype(np.float64)
+            assert f[0] == 1.0
+            ratio = f0[-1] / f[-1]
+            assert abs(ratio / (L / Lt) - 1.0) < 4 * 2.0 ** -24, (D, L, Lt, ratio)
+            # every other frequency is divided by less than the ratio (high frequencies extrapolate)
+            assert np.all(f0[1:-1] / f[1:-1] < L / Lt) and np.all(f0[1:] / f[1:] > 1.0)
+
+
 # --------------------------------------------------------------------------- segments and angles
 def test_segment_ids_hand():
     assert orc.segment_ids([2, 3, 1]).tolist() == [0, 0, 1, 1, 1, 2]
