@@ -41,7 +41,8 @@ struct KvCacheArgs {
 };
 
 // K and V are read with load_stream: each byte is read once, and the table rows that the
-// other heads of the token re-read stay cached.
+// other heads of the token re-read stay cached.  The cache rows are written with store_stream
+// (nothing here reads them back).
 
 template <typename T, int NP>
 __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
@@ -91,8 +92,8 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
         for (int p = 0; p < NP; ++p) {
             const int c = lane + p * G;
             if (c < nchunk) {
-                store_chunk<T>(vdst + c * 8, vx[p]);
-                store_chunk<T>(vdst + c * 8 + half, vy[p]);
+                store_stream<T>(vdst + c * 8, vx[p]);
+                store_stream<T>(vdst + c * 8 + half, vy[p]);
             }
         }
     }
@@ -138,8 +139,8 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(KvCacheArgs a) {
             } else {
                 rotate_pair(x[p], y[p], c0, s0, c1, s1);
             }
-            store_chunk<T>(kdst + c * 8, pack<T>(x[p]));
-            store_chunk<T>(kdst + c * 8 + half, pack<T>(y[p]));
+            store_stream<T>(kdst + c * 8, pack<T>(x[p]));
+            store_stream<T>(kdst + c * 8 + half, pack<T>(y[p]));
         }
     }
 }
