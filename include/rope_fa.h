@@ -158,7 +158,10 @@ rope_status rope_tables_ex(const int32_t* pos, const float* inv_freq, const int3
  * covers BNSD ([B, H, S, D], the input_layout of the [RoPE-fusion blog], section 三) and
  * BSND.  Packed varlen batches (cu_seqlens != NULL): token s of sequence b is packed row
  * t = cu_seqlens[b] + s at base + t*stride[1] + h*stride[2] + d*stride[3]; stride[0] is
- * ignored.  stride[3] (the head_dim stride) must be 1.  Strides are in elements.
+ * ignored.  stride[3] (the head_dim stride) must be 1.  Strides are in elements.  The
+ * attention calls (forward and backward) return ROPE_ERR_LIMIT when a K or V token stride
+ * (stride[1]) is 2^26 bytes or more: the fused kernel addresses its key tiles with 32-bit
+ * per-lane offsets.
  *
  * Tables (cos, sin) are [rows, head_dim] of table_dtype, row-major and contiguous, as
  * rope_tables writes them.  Row of token (b, s):

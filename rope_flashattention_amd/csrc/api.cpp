@@ -38,6 +38,8 @@ bool valid_dtype(rope_dtype dt) { return dt == ROPE_DT_F16 || dt == ROPE_DT_BF16
 
 bool valid_pairing(rope_pairing pr) { return pr == ROPE_PAIR_HALF || pr == ROPE_PAIR_INTERLEAVED; }
 
+constexpr int64_t kMaxTokenStrideBytes = (int64_t)1 << 26;
+
 // Strides {batch, token, head, dim}: dim must be 1; the others non-negative and 16-byte multiples.
 rope_status check_strides(const int64_t s[4], int elem_bytes, bool varlen) {
     if (s[3] != 1) return ROPE_ERR_UNSUPPORTED;
@@ -107,6 +109,10 @@ rope_status check_params(const rope_attn_params* p, bool attention) {
     if (attention) {
         if ((st = check_strides(p->v_stride, eb, varlen)) != ROPE_OK) return st;
         if ((st = check_strides(p->o_stride, eb, varlen)) != ROPE_OK) return st;
+        // the fused kernel addresses each 64-key K/V tile as a base pointer plus 32-bit
+        // per-lane byte offsets, so a K or V token stride must stay below 2^26 bytes
+        if (p->k_stride[1] * eb >= kMaxTokenStrideBytes || p->v_stride[1] * eb >= kMaxTokenStrideBytes)
+            return ROPE_ERR_LIMIT;
     }
     if (!aligned16(p->q) || !aligned16(p->k)) return ROPE_ERR_UNSUPPORTED;
     if (attention && (!aligned16(p->v) || !aligned16(p->out))) return ROPE_ERR_UNSUPPORTED;

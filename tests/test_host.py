@@ -181,6 +181,9 @@ BAD_COMMON = [
     (dict(softmax_scale=0.0), "ROPE_ERR_SHAPE"),
     (dict(softmax_scale=float("inf")), "ROPE_ERR_SHAPE"),
     (dict(o_stride=(8 * 100 * 128, 128, 100 * 128, 3)), "ROPE_ERR_UNSUPPORTED"),
+    # key tiles are addressed with 32-bit per-lane offsets: token strides below 2^26 bytes
+    (dict(k_stride=(0, 1 << 25, 128, 1)), "ROPE_ERR_LIMIT"),
+    (dict(v_stride=(0, 1 << 25, 128, 1)), "ROPE_ERR_LIMIT"),
     (dict(out=FAKE + 8), "ROPE_ERR_UNSUPPORTED"),
     (dict(lse=FAKE + 2), "ROPE_ERR_UNSUPPORTED"),
     (dict(cu_seqlens=FAKE, max_seqlen=0), "ROPE_ERR_SHAPE"),
