@@ -322,6 +322,9 @@ def test_bwd_rejects_forward_fields(ropelib):
     assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_ABI"]
     p = valid_bwd_params(D=96)
     assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_UNSUPPORTED"]
+    p = valid_bwd_params()
+    p.fwd.v_stride[1] = 1 << 25  # a V token stride of 2^26 bytes (bf16)
+    assert ropelib.rope_flash_attn_bwd(ctypes.byref(p), None) == ST["ROPE_ERR_LIMIT"]
     assert ropelib.rope_flash_attn_bwd(None, None) == ST["ROPE_ERR_NULL"]
 
 
