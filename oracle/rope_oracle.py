@@ -76,7 +76,8 @@ DTYPE_FORMATS = {"f16": (11, -14), "bf16": (8, -126), "f32": (24, -126)}
 def inv_freq(base: float, head_size: int) -> np.ndarray:
     """Inverse frequencies f_i = base^(-2i/D) for i < D/2, as float32.
 
-    [RoPE-fusion blog, section 1.2 snippet]: freqs = 1 / base ** (arange(0, D, 2) / D).
+    [RoPE-fusion blog, section 1.2]: frequency i is the reciprocal of base raised to the
+    power 2i/D, for the even dimension indices 2i < D.
     Formed in float64 and rounded once to float32, since the table op takes its
     inverse frequencies as a float32 input ([DynamicNTKOperation, 输入 table]).
     """
@@ -133,8 +134,8 @@ def segment_starts(seq_lens) -> np.ndarray:
 def angles(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32") -> np.ndarray:
     """freq[t, i] = (pos[t] / s) * f[b(t), i], the outer product per sequence.
 
-    [DynamicNTKOperation, 算子功能分析]: for each batch, freq = einsum('i,j->ij',
-    positionIds, invFreq).  The linear ``rope_scaling_factor`` s of [RoPE-fusion blog,
+    [DynamicNTKOperation, 算子功能分析]: for each batch, the outer product of that batch's
+    position ids with its row of inverse frequencies.  The linear ``rope_scaling_factor`` s of [RoPE-fusion blog,
     section 5.3] divides positions before the outer product.
 
     mode "fp32": the division and the product are each rounded to float32, as they
@@ -185,8 +186,9 @@ def pair_partner(D: int, pairing: str = "half"):
 def rope_tables(pos, inv_freq_b, seq_lens, pos_scale: float = 1.0, mode: str = "fp32", pairing: str = "half"):
     """(sin, cos), each float64 [ntokens, D].
 
-    [DynamicNTKOperation, 算子功能分析]: emb = cat((freq, freq), -1); sinOut = emb.sin();
-    cosOut = emb.cos().  Output shape [ntokens, headSize] ([输出]).  With
+    [DynamicNTKOperation, 算子功能分析]: the sine and the cosine of the angle matrix placed
+    twice side by side along the last axis (column j and column j + D/2 hold angle j).
+    Output shape [ntokens, headSize] ([输出]).  With
     pairing="interleaved" column j holds the angle of frequency j // 2 instead.
     """
     freq = angles(pos, inv_freq_b, seq_lens, pos_scale, mode)
