@@ -91,7 +91,7 @@ typedef enum rope_angle_mode {
  * rope_inv_freq — host-side inverse frequencies, one row per sequence.
  *
  * out[b, i] = fl32(1 / base_b ** (2i / head_size)), i < head_size/2
- * ([RoPE-fusion blog], section 1.2 snippet: freqs = 1/(base**(arange(0,D,2)/D))),
+ * ([RoPE-fusion blog], section 1.2: frequency i is 1 / base^(2i/D) for even indices 2i < D),
  * formed in double precision and rounded once to float.
  * base_b = base when trained_len <= 0 or seq_lens[b] <= trained_len; otherwise the
  * dynamic-NTK enlarged base base * (seq_lens[b] / trained_len) ** (D / (D - 2))
@@ -113,8 +113,8 @@ rope_status rope_inv_freq(double base, int32_t head_size, const int32_t* seq_len
  * rope_tables — the cos/sin tables of the DynamicNTK op ([DynamicNTKOperation],
  * 算子功能分析): for each sequence b and each of its tokens t,
  *   freq[t, i] = fl32(fl32(pos[t] / pos_scale) * inv_freq[b, i]),   i < head_size/2
- *   emb = cat(freq, freq);  sin_out[t, :] = sin(emb);  cos_out[t, :] = cos(emb)
- * rounded to nearest-even into out_dtype (fp16 subnormals kept).  pos_scale is the
+ *   sin_out[t, j] = sin(freq[t, j mod head_size/2]),  cos_out[t, j] = cos(freq[t, j mod head_size/2])
+ * (each angle fills column j and column j + head_size/2), rounded to nearest-even into out_dtype (fp16 subnormals kept).  pos_scale is the
  * linear rope_scaling_factor of the [RoPE-fusion blog], section 5.3 (positions are
  * divided by it before the outer product; 1.0f = no scaling).
  *
@@ -248,6 +248,12 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
  * formed in the kernel from pos and inv_freq (see the parameters).
  * Supported: head_dim 64 or 128 with F16, BF16 (fp16/bf16 matrix cores with float32
  * accumulation); head_dim 64 with F32 (float32 matrix cores).  Optional lse output (see above).
+ * Varlen lengths live on the device and are not validated; the kernels clamp them instead
+ * ([DynamicNTKOperation], 约束说明, requires positive lengths that sum to ntokens): sequence b
+ * covers the packed rows [s_b, s_b + L_b) with s_b = min(max(cu_seqlens[b], 0), ntokens) and
+ * L_b = max(0, min(cu_seqlens[b + 1] - s_b, max_seqlen, ntokens - s_b)), and is computed as a
+ * sequence of L_b tokens.  No access leaves the packed rows; rows of out and lse outside
+ * every such range are left unwritten.  With well-formed cu_seqlens nothing is clamped.
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
  */
 rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream);
@@ -294,7 +300,9 @@ uint64_t rope_flash_attn_bwd_workspace_size(const rope_attn_bwd_params* p);
  * The [FlashAttention blog] states that the operator serves training; the gradients are
  * those of the forward definition.  P is recomputed from the forward's lse, never stored.
  * Supported: F16/BF16, head_dim 64 or 128, causal or not, dense or varlen, GQA, both
- * pairings.  float32 accumulation; outputs rounded once to dtype.
+ * pairings.  float32 accumulation; outputs rounded once to dtype.  Varlen lengths are
+ * clamped exactly as in rope_flash_attn_fwd; rows of dq, dk, dv outside every clamped
+ * sequence are left unwritten.
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, WORKSPACE, HIP.  Three kernel launches
  * (row deltas with the rotated q', k'; dk/dv; dq).
  */

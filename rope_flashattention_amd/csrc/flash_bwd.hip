@@ -55,6 +55,7 @@ struct BwdArgs {
     int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // {batch, token, head}
     int32_t batch, hq, hkv, group, seqlen, table_seq_rows, lse_stride, causal;
     int32_t rows;                // query rows in total (dense batch*seqlen, varlen ntokens)
+    int32_t max_seqlen;          // varlen: host bound of every sequence length (the grid covers it)
     int32_t kv_tiles, q_tiles;   // 128-key tiles (dK/dV grid) and query tiles (dQ grid) per sequence
     float scale, scale_log2;
 };
@@ -120,8 +121,11 @@ __device__ __forceinline__ BwdSeq bwd_seq(const BwdArgs& a, int b) {
     BwdSeq s;
     int64_t ib, it;
     if (a.cu_seqlens) {
-        const int s0 = a.cu_seqlens[b];
-        s.L = a.cu_seqlens[b + 1] - s0;
+        // device-held lengths are clamped: rows stay inside the packed rows and the grid
+        const int64_t c0 = min(max((int64_t)a.cu_seqlens[b], (int64_t)0), (int64_t)a.rows);
+        const int64_t len = (int64_t)a.cu_seqlens[b + 1] - c0;
+        const int s0 = (int)c0;
+        s.L = (int)max((int64_t)0, min(len, min((int64_t)a.max_seqlen, (int64_t)a.rows - c0)));
         s.tok = s0;
         s.tab = s0;
         ib = 0;
@@ -785,6 +789,7 @@ hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream) {
     a.seqlen = varlen ? 0 : f->seqlen;
     a.table_seq_rows = f->table_seq_rows;
     a.rows = varlen ? f->ntokens : f->batch * f->seqlen;
+    a.max_seqlen = varlen ? f->max_seqlen : f->seqlen;
     a.lse_stride = a.rows;
     a.causal = f->causal;
     a.scale = f->softmax_scale;

@@ -54,6 +54,7 @@ struct FaArgs {
     const int32_t* cu_seqlens;  // nullptr: dense
     int64_t qs[3], ks[3], vs[3], os[3];  // {batch, token, head} strides in elements
     int32_t seqlen;                      // dense sequence length
+    int32_t ntokens, max_seqlen;         // varlen: packed rows in total and the host bound of every length
     int32_t group;                       // hq / hkv
     int32_t table_seq_rows;
     int32_t lse_stride;                  // tokens per lse row
@@ -151,8 +152,12 @@ __device__ __forceinline__ SeqView seq_view(const FaArgs& a, int b) {
     sv.seq_start = 0;
     sv.L = a.seqlen;
     if (sv.varlen) {
-        sv.seq_start = a.cu_seqlens[b];
-        sv.L = a.cu_seqlens[b + 1] - sv.seq_start;
+        // device-held lengths are clamped so that every row stays inside the packed rows
+        // and inside the grid (which covers max_seqlen rows per sequence)
+        const int64_t s0 = min(max((int64_t)a.cu_seqlens[b], (int64_t)0), (int64_t)a.ntokens);
+        const int64_t len = (int64_t)a.cu_seqlens[b + 1] - s0;
+        sv.seq_start = (int)s0;
+        sv.L = (int)max((int64_t)0, min(len, min((int64_t)a.max_seqlen, (int64_t)a.ntokens - s0)));
     }
     sv.qbase = sv.varlen ? (int64_t)sv.seq_start * a.qs[1] : (int64_t)b * a.qs[0];
     sv.kbase = sv.varlen ? (int64_t)sv.seq_start * a.ks[1] : (int64_t)b * a.ks[0];

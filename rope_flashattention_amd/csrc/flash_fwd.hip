@@ -43,6 +43,8 @@ hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream) {
     }
     const bool varlen = p->cu_seqlens != nullptr;
     a.seqlen = varlen ? 0 : p->seqlen;
+    a.ntokens = varlen ? p->ntokens : p->batch * p->seqlen;
+    a.max_seqlen = varlen ? p->max_seqlen : p->seqlen;
     a.group = p->hq / p->hkv;
     a.table_seq_rows = p->table_seq_rows;
     a.lse_stride = varlen ? p->ntokens : p->batch * p->seqlen;
