@@ -6,16 +6,19 @@ rope_tables (cos/sin for positions 0..S-1) followed by rope_flash_attn_fwd (rota
 Q/K in registers, causal attention).  The host inverse frequencies are computed once at
 set-up (a model-load-time quantity).  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
 
-The value is TFLOP/s of causal attention (4*B*Hq*S^2*D/2 per step) over the timed
-steps.  The roofline object reports the attention kernel's own time, measured with HIP
-events on the stream it runs on, against the dense bf16 MFMA peak.  Extra measurements
-(after the timed region): rope_tables GB/s at the op's size limits, rope_qk GB/s on the
-workload, the unfused path (rope_qk + attention without rotation) for the fusion
-ablation, the RoPE variants of the fused kernel, the backward pass, the fused RMSNorm +
-RoPE + KV-cache write GB/s on a paged-cache prefill, and decode-step attention GB/s over a
-paged cache.  The cpu_baseline leg times the fp64 CPU oracle on a bounded sample.
+The default workload is the largest single-GPU one: B1, 64 q heads over 8 kv heads,
+head_dim 128, S 16384, bf16, linear position scaling 2.  The value is TFLOP/s of causal
+attention (4*B*Hq*S^2*D/2 per step) over the timed steps.  The roofline object reports
+the attention kernel's own time, measured with HIP events on the stream it runs on,
+against the dense bf16 MFMA peak.  Extra measurements (after the timed region): the
+fusion ablation (fused kernel against rope_qk + attention without rotation, timed in
+alternating rounds after the same warm-up) on every 16-bit workload, rope_tables GB/s at
+the op's size limits, rope_qk GB/s, the RoPE variants of the fused kernel, the backward
+pass, the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill, and
+decode-step attention GB/s over a paged cache.  The cpu_baseline leg times the fp64 CPU
+oracle on a bounded sample of the same workload, phase by phase.
 """
 
 import argparse
@@ -101,52 +104,118 @@ def time_events(fn, reps, torch):
 
 
 def cpu_baseline(inp, budget_s):
-    """The oracle as it stands, one (sequence, q head) at a time, until the budget is spent."""
+    """The oracle as it stands, one (sequence, q head) at a time, until the budget is spent.
+
+    Each phase is timed on its own: the tables of the sequence (oracle.rope_tables), the
+    rotation of the head's queries and of its kv head's keys (oracle.rotate_tokens) and the
+    attention with the full N x N score matrix (oracle.attention)."""
     import numpy as np
     import oracle as orc
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing
+        blas = None
+    cores = len(os.sched_getaffinity(0))
     w = inp.workload
     q, k, v = inp.packed()
     starts = orc.segment_starts(inp.seq_lens)
     g = w.hq // w.hkv
+    phase = {"tables_s": 0.0, "rotation_s": 0.0, "attention_s": 0.0}
     t0 = time.perf_counter()
     flops, done = 0.0, 0
     for b in range(w.batch):
         s0, S = int(starts[b]), int(inp.seq_lens[b])
+        sl = slice(s0, s0 + S)
+        ta = time.perf_counter()
         f = orc.inv_freq_per_sequence(w.base, inp.seq_lens[b:b + 1], w.head_dim, w.trained_len)
-        sn, cs = orc.rope_tables(inp.pos[s0:s0 + S], f, inp.seq_lens[b:b + 1], w.pos_scale)
+        sn, cs = orc.rope_tables(inp.pos[sl], f, inp.seq_lens[b:b + 1], w.pos_scale)
         sn, cs = orc.round_rne(sn, w.dtype), orc.round_rne(cs, w.dtype)
+        phase["tables_s"] += time.perf_counter() - ta
         for h in range(w.hq):
-            sl = slice(s0, s0 + S)
-            orc.rope_attention(q[sl, h:h + 1], k[sl, h // g:h // g + 1], v[sl, h // g:h // g + 1], cs, sn, [S],
-                               w.softmax_scale, w.causal)
+            ta = time.perf_counter()
+            qr = orc.rotate_tokens(q[sl, h:h + 1], cs, sn)[:, 0]
+            kr = orc.rotate_tokens(k[sl, h // g:h // g + 1], cs, sn)[:, 0]
+            tb = time.perf_counter()
+            orc.attention(qr, kr, v[sl, h // g], w.softmax_scale, w.causal)
+            tc = time.perf_counter()
+            phase["rotation_s"] += tb - ta
+            phase["attention_s"] += tc - tb
             flops += 4.0 * S * S * w.head_dim / (2.0 if w.causal else 1.0)
             done += 1
-            if time.perf_counter() - t0 > budget_s:
+            if tc - t0 > budget_s:
                 break
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.batch * w.hq} (sequence, q head) pairs in order, full causal rows, "
-                      f"tables included; {dt:.1f} s wall, numpy float64 with {threads} BLAS threads"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": blas, "phases_s": {k2: round(v2, 3) for k2, v2 in phase.items()},
+            "sample": f"{done} of {w.batch * w.hq} (sequence, q head) pairs of {w.name} in order, full causal "
+                      f"rows, tables and rotation included; {dt:.1f} s wall on {cores} usable cores, numpy "
+                      f"float64 with {blas} BLAS threads (the exponentials run on one core)"}
+
+
+def attention_setup(w, inp, dev, rfa, wl, np, torch):
+    """Inputs resident in HBM, the host inverse frequencies, table and output buffers."""
+    D = w.head_dim
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    if w.varlen:
+        f = torch.from_numpy(rfa.inv_freq(w.base, D, inp.seq_lens, w.trained_len)).to(dev)
+        pos = torch.from_numpy(inp.pos).to(dev)
+        tab_lens = inp.seq_lens
+        cu = torch.from_numpy(wl.cu_seqlens(inp.seq_lens)).to(dev)
+        akw = dict(layout="TND", cu_seqlens=cu, max_seqlen=int(inp.seq_lens.max()))
+    else:
+        f = torch.from_numpy(rfa.inv_freq(w.base, D, [w.seqlen], w.trained_len)).to(dev)
+        pos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)   # one table shared by the batch
+        tab_lens = np.array([w.seqlen], dtype=np.int32)
+        akw = dict(layout="BNSD")
+    T_tab = int(tab_lens.sum())
+    sin = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
+    cos = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
+    out = torch.empty_like(q)
+    return dict(q=q, k=k, v=v, f=f, pos=pos, tab_lens=tab_lens, sin=sin, cos=cos, out=out, akw=akw)
+
+
+def fusion_ablation(w, st, rfa, torch, rounds=5, reps=10):
+    """Fused attention against the unfused path (rope_qk, then attention without rotation),
+    timed in alternating rounds of back-to-back launches after the same warm-up, so that
+    both legs see the same clock state.  Returns medians over the rounds (ms)."""
+    q, k, v, cos, sin, out, akw = st["q"], st["k"], st["v"], st["cos"], st["sin"], st["out"], st["akw"]
+    qkw = {kk: vv for kk, vv in akw.items()}
+    oq, ok = torch.empty_like(q), torch.empty_like(k)
+    fused = lambda: rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
+                                            out=out, **akw)
+    rot = lambda: rfa.rope_qk(q, k, cos, sin, table_seq_rows=0, out_q=oq, out_k=ok, **qkw)
+    plain = lambda: rfa.rope_flash_attn_fwd(oq, ok, v, None, None, causal=w.causal, softmax_scale=w.softmax_scale,
+                                            out=out, **akw)
+    rot()
+    for _ in range(reps):
+        fused()
+        plain()
+    tf, tr, tp = [], [], []
+    for _ in range(rounds):
+        tf.append(time_events(fused, reps, torch))
+        tr.append(time_events(rot, reps, torch))
+        tp.append(time_events(plain, reps, torch))
+    del oq, ok
+    mf, mr, mp = median(tf), median(tr), median(tp)
+    return {"fused_ms": round(mf, 4), "rope_qk_ms": round(mr, 4), "plain_attention_ms": round(mp, 4),
+            "unfused_ms": round(mr + mp, 4), "fused_over_unfused": round(mf / (mr + mp), 4)}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the GPU reaches its steady clocks only after ~100 ms of sustained work: 500 untimed
-    # steps of the benchmarked workload (about 0.1 s) before the K timed ones
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: the S=2048 MHA workload)")
+    ap.add_argument("--steps", type=int, default=20)
+    # the GPU reaches its steady clocks only after ~100 ms of sustained work: 50 untimed
+    # steps of the default workload (about 0.2 s) before the K timed ones
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload 1..5 (default 5: B1 H64/8 S16384, the largest single-GPU workload)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the table/rope_qk/unfused measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the measurements after the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -180,23 +249,9 @@ def main():
     D = w.head_dim
 
     # ---- set-up: inputs resident in HBM, host inverse frequencies, output buffers
-    if w.varlen:
-        q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
-        f = torch.from_numpy(rfa.inv_freq(w.base, D, inp.seq_lens, w.trained_len)).to(dev)
-        pos = torch.from_numpy(inp.pos).to(dev)
-        tab_lens = inp.seq_lens
-        cu = torch.from_numpy(wl.cu_seqlens(inp.seq_lens)).to(dev)
-        akw = dict(layout="TND", cu_seqlens=cu, max_seqlen=int(inp.seq_lens.max()))
-    else:
-        q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
-        f = torch.from_numpy(rfa.inv_freq(w.base, D, [w.seqlen], w.trained_len)).to(dev)
-        pos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)   # one table shared by the batch
-        tab_lens = np.array([w.seqlen], dtype=np.int32)
-        akw = dict(layout="BNSD")
-    T_tab = int(tab_lens.sum())
-    sin = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
-    cos = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
-    out = torch.empty_like(q)
+    st = attention_setup(w, inp, dev, rfa, wl, np, torch)
+    q, k, v, f, pos, tab_lens = st["q"], st["k"], st["v"], st["f"], st["pos"], st["tab_lens"]
+    sin, cos, out, akw = st["sin"], st["cos"], st["out"], st["akw"]
 
     def step():
         rfa.rope_tables(pos, f, tab_lens, D, w.pos_scale, w.torch_dtype, sin, cos)
@@ -256,7 +311,7 @@ def main():
                    "ntk_trained_len": w.trained_len, "pos_scale": w.pos_scale, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": read_traffic(wkey),
-                     "kernel": "flash_fwd_kernel", "avg_launch_ms": round(att_ms, 4)},
+                     "kernel": "flash_fwd16_kernel", "avg_launch_ms": round(att_ms, 4)},
         "components": {"rope_tables_ms": round(tab_ms, 5), "attention_ms": round(att_ms, 4),
                        "attention_ms_p10_median_p90": [round(att_all[int(0.1 * (K - 1))], 4),
                                                        round(median(att_all), 4),
@@ -274,28 +329,39 @@ def main():
     if not args.no_extras:
         comp = result["components"]
         # rope_qk on the workload (reads Q, K; writes Q', K'; table rows read once)
-        if w.varlen:
-            qkw = dict(layout="TND", cu_seqlens=akw["cu_seqlens"], max_seqlen=akw["max_seqlen"])
-            sq, cq = sin, cos
-            tsr = 0
-        else:
-            qkw = dict(layout="BNSD")
-            sq, cq, tsr = sin, cos, 0
         oq, ok = torch.empty_like(q), torch.empty_like(k)
-        qk_fn = lambda: rfa.rope_qk(q, k, cq, sq, table_seq_rows=tsr, out_q=oq, out_k=ok, **qkw)
+        qk_fn = lambda: rfa.rope_qk(q, k, cos, sin, table_seq_rows=0, out_q=oq, out_k=ok, **akw)
         for _ in range(3):
             qk_fn()
         ms = time_events(qk_fn, 20, torch)
-        qk_bytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * sq.numel() * sq.element_size()
+        qk_bytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * sin.numel() * sin.element_size()
         comp["rope_qk_ms"] = round(ms, 4)
         comp["rope_qk_gbps"] = round(qk_bytes / (ms * 1e-3) / 1e9, 1)
         comp["rope_qk_hbm_frac"] = round(qk_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        # fusion ablation: unfused = rope_qk + attention on the rotated tensors
-        ms_plain = time_events(lambda: rfa.rope_flash_attn_fwd(oq, ok, v, None, None, causal=w.causal,
-                                                               softmax_scale=w.softmax_scale, out=out, **akw), 10, torch)
-        comp["unfused_ms"] = round(ms + ms_plain, 4)
-        comp["fused_ms"] = round(att_ms, 4)
         del oq, ok
+        # fusion ablation on every 16-bit workload (this one first), and the attention
+        # throughput of the others
+        abl = {}
+        for c in [args.config] + [c for c in (2, 3, 4, 5) if c != args.config]:
+            wc = wl.CONFIGS[c]
+            if wc.dtype == "f32":
+                continue
+            if c == args.config:
+                sc, fl = st, flops
+            else:
+                ic = wl.generate(wc)
+                sc = attention_setup(wc, ic, dev, rfa, wl, np, torch)
+                rfa.rope_tables(sc["pos"], sc["f"], sc["tab_lens"], wc.head_dim, wc.pos_scale, wc.torch_dtype,
+                                sc["sin"], sc["cos"])
+                fl = wl.causal_flops(wc, ic.seq_lens)
+            r = fusion_ablation(wc, sc, rfa, torch)
+            r["fused_tflops"] = round(fl / (r["fused_ms"] * 1e-3) / 1e12, 2)
+            r["plain_attention_tflops"] = round(fl / (r["plain_attention_ms"] * 1e-3) / 1e12, 2)
+            abl[f"cfg{c}"] = r
+            if c != args.config:
+                del sc
+                torch.cuda.empty_cache()
+        comp["fusion_ablation"] = abl
         # backward on the same workload (delta, dk/dv and dq kernels; dO seeded): algorithmic
         # FLOPs 2.5x the forward's (the five products S, dP, dV, dK, dQ; the dq kernel's
         # recomputation of S and dP is overhead, not counted)
