@@ -450,6 +450,26 @@ rope_status rope_decode_attn_fwd(const rope_decode_params* p, void* hip_stream);
 /* sizeof(rope_decode_params) as compiled into the library (for bindings to check). */
 uint32_t rope_decode_params_size(void);
 
+/* Largest scratch rope_decode_attn_fwd_noalloc can use: 16 MiB per GPU. */
+#define ROPE_DECODE_NOALLOC_MAX_BYTES ((uint64_t)16 << 20)
+
+/*
+ * rope_decode_attn_fwd_noalloc — rope_decode_attn_fwd for callers that cannot allocate
+ * device memory or set up a workspace per call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same computation, same kernels and the same
+ * result bit for bit; p->workspace and p->workspace_bytes are ignored.  The split partials
+ * go to a scratch array of ROPE_DECODE_NOALLOC_MAX_BYTES that the library holds on every GPU
+ * it runs on until the process ends; a call whose rope_decode_workspace_size exceeds it
+ * returns ROPE_ERR_LIMIT (fewer num_splits reduce the need).  The entry point allocates
+ * nothing: the scratch address is looked up (hipGetSymbolAddress) on the first call on each
+ * device.  hip_stream must belong to the current device (else ROPE_ERR_HIP).  Every call on
+ * one GPU shares that GPU's scratch: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller; calls in order on one stream
+ * are safe.  Nothing in the scratch needs clearing between calls.
+ * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  Two kernel launches.
+ */
+rope_status rope_decode_attn_fwd_noalloc(const rope_decode_params* p, void* hip_stream);
+
 /* Static text for a status code ("ROPE_OK", ...); never NULL. */
 const char* rope_status_str(rope_status s);
 

@@ -211,6 +211,8 @@ def lib() -> ctypes.CDLL:
     L.rope_kv_cache_params_size.restype = ctypes.c_uint32
     L.rope_decode_attn_fwd.argtypes = [ctypes.POINTER(RopeDecodeParams), vp]
     L.rope_decode_attn_fwd.restype = st
+    L.rope_decode_attn_fwd_noalloc.argtypes = [ctypes.POINTER(RopeDecodeParams), vp]
+    L.rope_decode_attn_fwd_noalloc.restype = st
     L.rope_decode_workspace_size.argtypes = [ctypes.POINTER(RopeDecodeParams)]
     L.rope_decode_workspace_size.restype = ctypes.c_uint64
     L.rope_decode_params_size.restype = ctypes.c_uint32
@@ -632,3 +634,27 @@ def rope_decode_attn_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         p.lse = lse.data_ptr()
     _check("rope_decode_attn_fwd", lib().rope_decode_attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def rope_decode_attn_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 cache_seqlens: torch.Tensor, cos: Optional[torch.Tensor] = None,
+                                 sin: Optional[torch.Tensor] = None, *, max_seqlen: int, out: torch.Tensor,
+                                 lse: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                                 softmax_scale: Optional[float] = None, cache_layout: str = "BSND",
+                                 num_splits: int = 0, pairing: str = "half") -> torch.Tensor:
+    """rope_decode_attn_fwd through the allocation-free entry point: nothing is allocated,
+    here or in the library (the split partials use the library's per-GPU scratch).  The
+    caller passes out (like q) and, if wanted, lse (contiguous float32 [batch, hq])."""
+    _need_cuda(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, out, lse)
+    p = _decode_params(q, k_cache, v_cache, cache_seqlens, cos, sin, block_table, max_seqlen, softmax_scale,
+                       cache_layout, num_splits, pairing)
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(2) != 1:
+        raise ValueError("out must match q")
+    p.out = out.data_ptr()
+    p.o_stride[:] = (out.stride(0), out.stride(1))
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:2]):
+            raise ValueError("lse must be contiguous float32 [batch, hq]")
+        p.lse = lse.data_ptr()
+    _check("rope_decode_attn_fwd_noalloc", lib().rope_decode_attn_fwd_noalloc(ctypes.byref(p), _stream(q)))
+    return out

@@ -26,6 +26,7 @@ hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream);
 uint64_t flash_bwd_workspace_bytes(const rope_attn_params* f);
 int decode_num_splits(const rope_decode_params* p);
 uint64_t decode_workspace_bytes(const rope_decode_params* p, int nsplit);
+hipError_t decode_scratch(hipStream_t stream, void** out);
 }  // namespace ropefa
 
 using ropefa::dtype_bytes;
@@ -210,7 +211,7 @@ rope_status check_decode_shape(const rope_decode_params* p) {
     return ROPE_OK;
 }
 
-rope_status check_decode(const rope_decode_params* p) {
+rope_status check_decode(const rope_decode_params* p, bool with_workspace = true) {
     rope_status st = check_decode_shape(p);
     if (st != ROPE_OK) return st;
     if (!valid_dtype(p->dtype)) return ROPE_ERR_DTYPE;
@@ -238,6 +239,7 @@ rope_status check_decode(const rope_decode_params* p) {
     if ((reinterpret_cast<uintptr_t>(p->block_table) & 3u) || (reinterpret_cast<uintptr_t>(p->cache_seqlens) & 3u) ||
         (reinterpret_cast<uintptr_t>(p->lse) & 3u))
         return ROPE_ERR_UNSUPPORTED;
+    if (!with_workspace) return ROPE_OK;
     const uint64_t need = ropefa::decode_workspace_bytes(p, ropefa::decode_num_splits(p));
     if (!p->workspace || (reinterpret_cast<uintptr_t>(p->workspace) & 255u) || p->workspace_bytes < need)
         return ROPE_ERR_WORKSPACE;
@@ -364,6 +366,21 @@ rope_status rope_decode_attn_fwd(const rope_decode_params* p, void* hip_stream) 
     const rope_status st = check_decode(p);
     if (st != ROPE_OK) return st;
     const hipError_t e = ropefa::launch_decode(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status rope_decode_attn_fwd_noalloc(const rope_decode_params* p, void* hip_stream) {
+    const rope_status st = check_decode(p, false);
+    if (st != ROPE_OK) return st;
+    if (ropefa::decode_workspace_bytes(p, ropefa::decode_num_splits(p)) > ROPE_DECODE_NOALLOC_MAX_BYTES)
+        return ROPE_ERR_LIMIT;
+    void* ws = nullptr;
+    hipError_t e = ropefa::decode_scratch((hipStream_t)hip_stream, &ws);
+    if (e != hipSuccess) return ROPE_ERR_HIP;
+    rope_decode_params q = *p;
+    q.workspace = ws;
+    q.workspace_bytes = ROPE_DECODE_NOALLOC_MAX_BYTES;
+    e = ropefa::launch_decode(&q, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 

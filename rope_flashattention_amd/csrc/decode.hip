@@ -36,6 +36,8 @@
 // The wave writes its unnormalised O, reference m and sum l for its key range to the
 // workspace.  Combine kernel (decode_combine_kernel): one workgroup per (sequence, q head)
 // merges the splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+#include <mutex>
+
 #include "common.h"
 
 namespace ropefa {
@@ -434,6 +436,41 @@ static void launch_typed(const DecodeArgs& a, hipStream_t stream) {
                                 : dim3(a.nsplit, a.hkv * a.ngroups, a.batch);
     hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(64), 0, stream, a);
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.batch * a.hq), dim3(D), 0, stream, a);
+}
+
+// ============================================================================ allocation-free entry
+// Scratch of rope_decode_attn_fwd_noalloc: the split partials (what rope_decode_attn_fwd keeps
+// in the caller's workspace) in a file-scope device array of a fixed size.  Every GPU the
+// library runs on holds its own copy, at its own address, until the process ends.  In host
+// code the array's name is only a stand-in: kernels and copies use the device address that
+// hipGetSymbolAddress returns, looked up once per device.  Nothing in the array must start at
+// zero (the partial kernel writes every split that holds keys, the combine kernel reads only
+// those), and every call on one GPU shares it, so calls that overlap on a GPU race.
+static __device__ __align__(256) unsigned char scratch[ROPE_DECODE_NOALLOC_MAX_BYTES];
+
+hipError_t decode_scratch(hipStream_t stream, void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (stream) {  // the scratch used is the current device's: the stream must belong to it
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipErrorInvalidDevice;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream) {

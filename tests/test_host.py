@@ -465,6 +465,30 @@ def test_decode_rejects(ropelib, kw, status):
     assert ropelib.rope_decode_attn_fwd(ctypes.byref(p), None) == ST[status]
 
 
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), "ROPE_ERR_ABI"),
+    (dict(dtype=0), "ROPE_ERR_DTYPE"),
+    (dict(q=None), "ROPE_ERR_NULL"),
+    (dict(out=None), "ROPE_ERR_NULL"),
+    (dict(hq=6), "ROPE_ERR_SHAPE"),
+    (dict(head_dim=96), "ROPE_ERR_UNSUPPORTED"),
+    (dict(num_splits=257), "ROPE_ERR_LIMIT"),
+    # beyond the 16 MiB scratch: 64 x 64 heads x 256 splits x (128 + 2) floats
+    (dict(batch=64, hq=64, hkv=8, num_blocks=64 * 64, num_splits=256), "ROPE_ERR_LIMIT"),
+])
+def test_decode_noalloc_rejects(ropelib, kw, status):
+    """The allocation-free decode entry validates like the workspace one (its workspace
+    fields are ignored) and rejects a call that needs more than its scratch, all on the host."""
+    p = mutate(valid_decode_params(), workspace=None, workspace_bytes=0, **kw)
+    assert ropelib.rope_decode_attn_fwd_noalloc(ctypes.byref(p), None) == ST[status]
+
+
+def test_decode_noalloc_scratch_limit_is_16_mib():
+    text = open(HEADER).read()
+    assert "#define ROPE_DECODE_NOALLOC_MAX_BYTES ((uint64_t)16 << 20)" in text
+
+
 def test_binding_refuses_cpu_tensors(ropelib):
     import torch
     q = torch.zeros(1, 4, 8, 64)
