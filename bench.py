@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "fused RoPE+FlashAttn fwd TFLOP/s and % bf16 MFMA peak; rope_tables GB/s"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA peaks (f32: matrix fp32)
 PEAK_HBM_GBS = 8000.0
+EXTRAS = ("ablation", "backward", "variants", "tables", "kvcache", "decode")
 KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.h", "rope_flashattention_amd/csrc/common.h"]
 
 
@@ -216,6 +217,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the measurements after the timed region")
+    ap.add_argument("--ablation-configs", default="2,3,4,5",
+                    help="workloads of the fusion ablation besides the benchmarked one (comma list, may be empty)")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma list of the measurements after the timed region (default all): " + ", ".join(EXTRAS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -326,155 +331,163 @@ def main():
         result["components"]["peak_at_max_clock_tflops"] = round(pk, 1)
         result["components"]["frac_of_peak_at_max_clock"] = round(achieved / pk, 4)
 
+    extras = set(args.extras.split(","))
     if not args.no_extras:
         comp = result["components"]
-        # rope_qk on the workload (reads Q, K; writes Q', K'; table rows read once)
-        oq, ok = torch.empty_like(q), torch.empty_like(k)
-        qk_fn = lambda: rfa.rope_qk(q, k, cos, sin, table_seq_rows=0, out_q=oq, out_k=ok, **akw)
-        for _ in range(3):
-            qk_fn()
-        ms = time_events(qk_fn, 20, torch)
-        qk_bytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * sin.numel() * sin.element_size()
-        comp["rope_qk_ms"] = round(ms, 4)
-        comp["rope_qk_gbps"] = round(qk_bytes / (ms * 1e-3) / 1e9, 1)
-        comp["rope_qk_hbm_frac"] = round(qk_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        del oq, ok
-        # fusion ablation on every 16-bit workload (this one first), and the attention
-        # throughput of the others
-        abl = {}
-        for c in [args.config] + [c for c in (2, 3, 4, 5) if c != args.config]:
-            wc = wl.CONFIGS[c]
-            if wc.dtype == "f32":
-                continue
-            if c == args.config:
-                sc, fl = st, flops
-            else:
-                ic = wl.generate(wc)
-                sc = attention_setup(wc, ic, dev, rfa, wl, np, torch)
-                rfa.rope_tables(sc["pos"], sc["f"], sc["tab_lens"], wc.head_dim, wc.pos_scale, wc.torch_dtype,
-                                sc["sin"], sc["cos"])
-                fl = wl.causal_flops(wc, ic.seq_lens)
-            r = fusion_ablation(wc, sc, rfa, torch)
-            r["fused_tflops"] = round(fl / (r["fused_ms"] * 1e-3) / 1e12, 2)
-            r["plain_attention_tflops"] = round(fl / (r["plain_attention_ms"] * 1e-3) / 1e12, 2)
-            abl[f"cfg{c}"] = r
-            if c != args.config:
-                del sc
-                torch.cuda.empty_cache()
-        comp["fusion_ablation"] = abl
-        # backward on the same workload (delta, dk/dv and dq kernels; dO seeded): algorithmic
-        # FLOPs 2.5x the forward's (the five products S, dP, dV, dK, dQ; the dq kernel's
-        # recomputation of S and dP is overhead, not counted)
-        if w.dtype != "f32":
-            out_f, lse_f = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
-                                                   return_lse=True, **akw)
-            bdo = wl.generate_dout(inp, 9001).to(dev)
-            if not w.varlen and akw.get("layout") == "BSND":
-                bdo = bdo.transpose(1, 2).contiguous()
-            bdq, bdk, bdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            bfn = lambda: rfa.rope_flash_attn_bwd(q, k, v, out_f, lse_f, bdo, cos, sin, causal=w.causal,
-                                                  softmax_scale=w.softmax_scale, dq=bdq, dk=bdk, dv=bdv, **akw)
-            bfn()
-            bms = time_events(bfn, 10, torch)
-            comp["bwd_ms"] = round(bms, 4)
-            comp["bwd_tflops"] = round(2.5 * flops / (bms * 1e-3) / 1e12, 2)
-            del out_f, lse_f, bdo, bdq, bdk, bdv
-        # RoPE variants of the fused kernel on the same workload: interleaved pairs (tables
-        # from rope_tables_ex), and table values formed inside the kernel (no table read, no
-        # table pass) for both pairings
-        if not w.varlen:
-            vpos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)
-            vf = torch.from_numpy(rfa.inv_freq(w.base, w.head_dim, [w.seqlen], w.trained_len)).to(dev)
-            isin, icos = rfa.rope_tables(vpos, vf, [w.seqlen], w.head_dim, w.pos_scale, w.torch_dtype,
-                                         pairing="interleaved")
-            vkw = dict(causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
-            for name, fn in (
-                    ("interleaved_tables", lambda: rfa.rope_flash_attn_fwd(q, k, v, icos, isin, pairing="interleaved",
-                                                                           **vkw)),
-                    ("formed_tables_half", lambda: rfa.rope_flash_attn_fwd(q, k, v, None, None, pos=vpos, inv_freq=vf,
-                                                                           pos_scale=w.pos_scale, **vkw)),
-                    ("formed_tables_interleaved", lambda: rfa.rope_flash_attn_fwd(
-                        q, k, v, None, None, pos=vpos, inv_freq=vf, pos_scale=w.pos_scale, pairing="interleaved",
-                        **vkw))):
-                fn()
-                vms = time_events(fn, 10, torch)
-                comp[f"fused_{name}_ms"] = round(vms, 4)
-                comp[f"fused_{name}_tflops"] = round(flops / (vms * 1e-3) / 1e12, 2)
-        # rope_tables at the op's limits: batch 16, ntokens 256000 (sequences of 16000 tokens),
-        # head_size 2048 (2.1 GB written) and 512
-        lens = np.full(16, 16000, dtype=np.int32)
-        tpos = torch.arange(16000, dtype=torch.int32, device=dev).repeat(16)
-        for Dt in (2048, 512):
-            tf = torch.from_numpy(rfa.inv_freq(1e4, Dt, lens, 4096)).to(dev)
-            variants = []
-            for dt_name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
-                ts = torch.empty((256000, Dt), dtype=dt, device=dev)
-                tc = torch.empty((256000, Dt), dtype=dt, device=dev)
-                variants.append((dt_name, (lambda ts=ts, tc=tc, dt=dt: rfa.rope_tables(tpos, tf, lens, Dt, 1.0, dt, ts,
-                                                                                      tc))))
-            # the dtypes are timed in turn, three times each, and the median taken: the first
-            # variant timed after the matrix-bound runs above otherwise reads up to 15% slow
-            times = {name: [] for name, _ in variants}
+        if "ablation" in extras:
+            # rope_qk on the workload (reads Q, K; writes Q', K'; table rows read once)
+            oq, ok = torch.empty_like(q), torch.empty_like(k)
+            qk_fn = lambda: rfa.rope_qk(q, k, cos, sin, table_seq_rows=0, out_q=oq, out_k=ok, **akw)
             for _ in range(3):
-                for name, fn in variants:
-                    for _ in range(10):
-                        fn()
-                    times[name].append(time_events(fn, 20, torch))
-            tb = 2 * 256000 * Dt * 2 + 4 * 256000 + 4 * 16 * (Dt // 2)
-            for name, _ in variants:
-                ms = median(times[name])
-                comp[f"rope_tables_{name}_T256000_D{Dt}_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
-                comp[f"rope_tables_{name}_T256000_D{Dt}_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-            del variants
-        torch.cuda.empty_cache()
-        # fused RMSNorm + RoPE + KV-cache write on a 16 x 4096-token prefill into a paged cache:
-        # reads K, V and the table rows, writes K', V into the cache (slots, gamma are small)
-        cw = wl.CACHE_CONFIGS["prefill"]
-        ci = wl.generate_cache(cw)
-        ck, cv = ci.k.to(dev), ci.v.to(dev)
-        kc, vc = ci.k_cache.to(dev), ci.v_cache.to(dev)
-        cgam, cslots = ci.gamma.to(dev), torch.from_numpy(ci.slots).to(dev)
-        clens = np.full(cw.batch, cw.new_tokens, dtype=np.int32)
-        cf = torch.from_numpy(rfa.inv_freq(cw.base, cw.head_dim, clens)).to(dev)
-        csin, ccos = rfa.rope_tables(torch.from_numpy(ci.pos).to(dev), cf, clens, cw.head_dim, 1.0, cw.torch_dtype)
-        fn = lambda: rfa.rope_kv_rms_norm_rope_cache(ck, cv, ccos, csin, cslots, kc, vc, gamma=cgam, eps=1e-6)
-        for _ in range(3):
-            fn()
-        ms = time_events(fn, 20, torch)
-        esz = ck.element_size()
-        cb = 4 * ck.numel() * esz + 2 * csin.numel() * esz + 8 * cslots.numel() + 4 * cgam.numel()
-        comp["kv_cache_workload"] = cw.name
-        comp["kv_cache_ms"] = round(ms, 4)
-        comp["kv_cache_gbps"] = round(cb / (ms * 1e-3) / 1e9, 1)
-        comp["kv_cache_hbm_frac"] = round(cb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        del ck, cv, kc, vc, ci
-        torch.cuda.empty_cache()
-        # decode step over a paged cache: 32 sequences with 1024..8192 cached tokens, Hq 64 / Hkv 8;
-        # both launches (split partials and their merge) inside the timed call
-        dw = wl.CACHE_CONFIGS["decode"]
-        di = wl.generate_cache(dw)
-        dlens = (di.ctx + 1).astype(np.int32)
-        dq = di.q.to(dev)
-        dkc, dvc = di.k_cache.to(dev), di.v_cache.to(dev)
-        dbt = torch.from_numpy(di.block_table.astype(np.int32)).to(dev)
-        dsl = torch.from_numpy(dlens).to(dev)
-        dfr = torch.from_numpy(rfa.inv_freq(dw.base, dw.head_dim)).to(dev)
-        dsin, dcos = rfa.rope_tables(torch.from_numpy(di.pos).to(dev), dfr, [dw.batch], dw.head_dim, 1.0,
-                                     dw.torch_dtype)
-        dkw = dict(max_seqlen=int(dlens.max()), block_table=dbt)
-        dws = torch.empty(rfa.decode_workspace_size(dq, dkc, dvc, dsl, **dkw), dtype=torch.uint8, device=dev)
-        dout = torch.empty_like(dq)
-        fn = lambda: rfa.rope_decode_attn_fwd(dq, dkc, dvc, dsl, dcos, dsin, out=dout, workspace=dws, **dkw)
-        for _ in range(3):
-            fn()
-        ms = time_events(fn, 20, torch)
-        db = wl.decode_bytes(dw, dlens)
-        comp["decode_workload"] = dw.name
-        comp["decode_ms"] = round(ms, 4)
-        comp["decode_gbps"] = round(db / (ms * 1e-3) / 1e9, 1)
-        comp["decode_hbm_frac"] = round(db / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        del dq, dkc, dvc, dws, di
-        torch.cuda.empty_cache()
+                qk_fn()
+            ms = time_events(qk_fn, 20, torch)
+            qk_bytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * sin.numel() * sin.element_size()
+            comp["rope_qk_ms"] = round(ms, 4)
+            comp["rope_qk_gbps"] = round(qk_bytes / (ms * 1e-3) / 1e9, 1)
+            comp["rope_qk_hbm_frac"] = round(qk_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del oq, ok
+            # fusion ablation on every 16-bit workload (this one first), and the attention
+            # throughput of the others
+            abl = {}
+            others = [int(c) for c in args.ablation_configs.split(",") if c and int(c) != args.config]
+            for c in [args.config] + others:
+                wc = wl.CONFIGS[c]
+                if wc.dtype == "f32":
+                    continue
+                if c == args.config:
+                    sc, fl = st, flops
+                else:
+                    ic = wl.generate(wc)
+                    sc = attention_setup(wc, ic, dev, rfa, wl, np, torch)
+                    rfa.rope_tables(sc["pos"], sc["f"], sc["tab_lens"], wc.head_dim, wc.pos_scale, wc.torch_dtype,
+                                    sc["sin"], sc["cos"])
+                    fl = wl.causal_flops(wc, ic.seq_lens)
+                r = fusion_ablation(wc, sc, rfa, torch)
+                r["fused_tflops"] = round(fl / (r["fused_ms"] * 1e-3) / 1e12, 2)
+                r["plain_attention_tflops"] = round(fl / (r["plain_attention_ms"] * 1e-3) / 1e12, 2)
+                abl[f"cfg{c}"] = r
+                if c != args.config:
+                    del sc
+                    torch.cuda.empty_cache()
+            comp["fusion_ablation"] = abl
+        if "backward" in extras:
+            # backward on the same workload (delta, dk/dv and dq kernels; dO seeded): algorithmic
+            # FLOPs 2.5x the forward's (the five products S, dP, dV, dK, dQ; the dq kernel's
+            # recomputation of S and dP is overhead, not counted)
+            if w.dtype != "f32":
+                out_f, lse_f = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
+                                                       return_lse=True, **akw)
+                bdo = wl.generate_dout(inp, 9001).to(dev)
+                if not w.varlen and akw.get("layout") == "BSND":
+                    bdo = bdo.transpose(1, 2).contiguous()
+                bdq, bdk, bdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                bfn = lambda: rfa.rope_flash_attn_bwd(q, k, v, out_f, lse_f, bdo, cos, sin, causal=w.causal,
+                                                      softmax_scale=w.softmax_scale, dq=bdq, dk=bdk, dv=bdv, **akw)
+                bfn()
+                bms = time_events(bfn, 10, torch)
+                comp["bwd_ms"] = round(bms, 4)
+                comp["bwd_tflops"] = round(2.5 * flops / (bms * 1e-3) / 1e12, 2)
+                del out_f, lse_f, bdo, bdq, bdk, bdv
+        if "variants" in extras:
+            # RoPE variants of the fused kernel on the same workload: interleaved pairs (tables
+            # from rope_tables_ex), and table values formed inside the kernel (no table read, no
+            # table pass) for both pairings
+            if not w.varlen:
+                vpos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)
+                vf = torch.from_numpy(rfa.inv_freq(w.base, w.head_dim, [w.seqlen], w.trained_len)).to(dev)
+                isin, icos = rfa.rope_tables(vpos, vf, [w.seqlen], w.head_dim, w.pos_scale, w.torch_dtype,
+                                             pairing="interleaved")
+                vkw = dict(causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+                for name, fn in (
+                        ("interleaved_tables", lambda: rfa.rope_flash_attn_fwd(q, k, v, icos, isin, pairing="interleaved",
+                                                                               **vkw)),
+                        ("formed_tables_half", lambda: rfa.rope_flash_attn_fwd(q, k, v, None, None, pos=vpos, inv_freq=vf,
+                                                                               pos_scale=w.pos_scale, **vkw)),
+                        ("formed_tables_interleaved", lambda: rfa.rope_flash_attn_fwd(
+                            q, k, v, None, None, pos=vpos, inv_freq=vf, pos_scale=w.pos_scale, pairing="interleaved",
+                            **vkw))):
+                    fn()
+                    vms = time_events(fn, 10, torch)
+                    comp[f"fused_{name}_ms"] = round(vms, 4)
+                    comp[f"fused_{name}_tflops"] = round(flops / (vms * 1e-3) / 1e12, 2)
+        if "tables" in extras:
+            # rope_tables at the op's limits: batch 16, ntokens 256000 (sequences of 16000 tokens),
+            # head_size 2048 (2.1 GB written) and 512
+            lens = np.full(16, 16000, dtype=np.int32)
+            tpos = torch.arange(16000, dtype=torch.int32, device=dev).repeat(16)
+            for Dt in (2048, 512):
+                tf = torch.from_numpy(rfa.inv_freq(1e4, Dt, lens, 4096)).to(dev)
+                variants = []
+                for dt_name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+                    ts = torch.empty((256000, Dt), dtype=dt, device=dev)
+                    tc = torch.empty((256000, Dt), dtype=dt, device=dev)
+                    variants.append((dt_name, (lambda ts=ts, tc=tc, dt=dt: rfa.rope_tables(tpos, tf, lens, Dt, 1.0, dt, ts,
+                                                                                          tc))))
+                # the dtypes are timed in turn, three times each, and the median taken: the first
+                # variant timed after the matrix-bound runs above otherwise reads up to 15% slow
+                times = {name: [] for name, _ in variants}
+                for _ in range(3):
+                    for name, fn in variants:
+                        for _ in range(10):
+                            fn()
+                        times[name].append(time_events(fn, 20, torch))
+                tb = 2 * 256000 * Dt * 2 + 4 * 256000 + 4 * 16 * (Dt // 2)
+                for name, _ in variants:
+                    ms = median(times[name])
+                    comp[f"rope_tables_{name}_T256000_D{Dt}_gbps"] = round(tb / (ms * 1e-3) / 1e9, 1)
+                    comp[f"rope_tables_{name}_T256000_D{Dt}_hbm_frac"] = round(tb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                del variants
+            torch.cuda.empty_cache()
+        if "kvcache" in extras:
+            # fused RMSNorm + RoPE + KV-cache write on a 16 x 4096-token prefill into a paged cache:
+            # reads K, V and the table rows, writes K', V into the cache (slots, gamma are small)
+            cw = wl.CACHE_CONFIGS["prefill"]
+            ci = wl.generate_cache(cw)
+            ck, cv = ci.k.to(dev), ci.v.to(dev)
+            kc, vc = ci.k_cache.to(dev), ci.v_cache.to(dev)
+            cgam, cslots = ci.gamma.to(dev), torch.from_numpy(ci.slots).to(dev)
+            clens = np.full(cw.batch, cw.new_tokens, dtype=np.int32)
+            cf = torch.from_numpy(rfa.inv_freq(cw.base, cw.head_dim, clens)).to(dev)
+            csin, ccos = rfa.rope_tables(torch.from_numpy(ci.pos).to(dev), cf, clens, cw.head_dim, 1.0, cw.torch_dtype)
+            fn = lambda: rfa.rope_kv_rms_norm_rope_cache(ck, cv, ccos, csin, cslots, kc, vc, gamma=cgam, eps=1e-6)
+            for _ in range(3):
+                fn()
+            ms = time_events(fn, 20, torch)
+            esz = ck.element_size()
+            cb = 4 * ck.numel() * esz + 2 * csin.numel() * esz + 8 * cslots.numel() + 4 * cgam.numel()
+            comp["kv_cache_workload"] = cw.name
+            comp["kv_cache_ms"] = round(ms, 4)
+            comp["kv_cache_gbps"] = round(cb / (ms * 1e-3) / 1e9, 1)
+            comp["kv_cache_hbm_frac"] = round(cb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del ck, cv, kc, vc, ci
+            torch.cuda.empty_cache()
+        if "decode" in extras:
+            # decode step over a paged cache: 32 sequences with 1024..8192 cached tokens, Hq 64 / Hkv 8;
+            # both launches (split partials and their merge) inside the timed call
+            dw = wl.CACHE_CONFIGS["decode"]
+            di = wl.generate_cache(dw)
+            dlens = (di.ctx + 1).astype(np.int32)
+            dq = di.q.to(dev)
+            dkc, dvc = di.k_cache.to(dev), di.v_cache.to(dev)
+            dbt = torch.from_numpy(di.block_table.astype(np.int32)).to(dev)
+            dsl = torch.from_numpy(dlens).to(dev)
+            dfr = torch.from_numpy(rfa.inv_freq(dw.base, dw.head_dim)).to(dev)
+            dsin, dcos = rfa.rope_tables(torch.from_numpy(di.pos).to(dev), dfr, [dw.batch], dw.head_dim, 1.0,
+                                         dw.torch_dtype)
+            dkw = dict(max_seqlen=int(dlens.max()), block_table=dbt)
+            dws = torch.empty(rfa.decode_workspace_size(dq, dkc, dvc, dsl, **dkw), dtype=torch.uint8, device=dev)
+            dout = torch.empty_like(dq)
+            fn = lambda: rfa.rope_decode_attn_fwd(dq, dkc, dvc, dsl, dcos, dsin, out=dout, workspace=dws, **dkw)
+            for _ in range(3):
+                fn()
+            ms = time_events(fn, 20, torch)
+            db = wl.decode_bytes(dw, dlens)
+            comp["decode_workload"] = dw.name
+            comp["decode_ms"] = round(ms, 4)
+            comp["decode_gbps"] = round(db / (ms * 1e-3) / 1e9, 1)
+            comp["decode_hbm_frac"] = round(db / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del dq, dkc, dvc, dws, di
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

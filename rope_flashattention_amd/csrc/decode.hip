@@ -367,35 +367,60 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(DecodeArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     // one workgroup of D threads per (sequence, q head); thread d owns output column d.
-    // The split statistics are read 64 at a time, one split per lane (each wave computes
-    // them redundantly), and the weighted sum over the splits issues its loads back to back.
+    // The split statistics are read one split per lane (each wave computes them
+    // redundantly).  With at most kPre splits (the usual case) every load of the kernel -
+    // the sequence length, the statistics and the partial rows - is issued at once, before
+    // the length says which splits hold keys, so the kernel waits for memory once; the
+    // partial rows of splits past the last live one are read (the workspace holds them,
+    // written or not) and dropped by a select, never by a multiply.
     constexpr float kNegInf = -__builtin_inff();
+    constexpr int kPre = 16;
     const int bh = blockIdx.x;
     const int b = bh / a.hq;
     const int h = bh - b * a.hq;
     const int d = threadIdx.x;
     const int lane = d & 63;
     const int64_t p0 = (int64_t)bh * a.nsplit;
-    const int live = (seq_len(a, b) + a.chunk - 1) / a.chunk;  // the splits the partial kernel wrote
-    float M = kNegInf;
-    for (int s0 = 0; s0 < live; s0 += 64) M = fmaxf(M, s0 + lane < live ? a.ws_m[p0 + s0 + lane] : kNegInf);
+    float o = 0.0f, lsum = 0.0f, M = kNegInf;
+    int live;
+    if (a.nsplit <= kPre) {
+        const int ls = min(lane, a.nsplit - 1);
+        const float mv = a.ws_m[p0 + ls];
+        const float lv = a.ws_l[p0 + ls];
+        float v[kPre];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float o = 0.0f, lsum = 0.0f;
-    for (int s0 = 0; s0 < live; s0 += 64) {
-        const int s = s0 + lane;
-        const float w = s < live ? exp2f(a.ws_m[p0 + s] - M) : 0.0f;
-        lsum += s < live ? w * a.ws_l[p0 + s] : 0.0f;
-        const int n = min(64, live - s0);
-        const float* wo = a.ws_o + (p0 + s0) * D + d;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-            float v[8];
+        for (int u = 0; u < kPre; ++u) v[u] = a.ws_o[(p0 + min(u, a.nsplit - 1)) * D + d];
+        live = (seq_len(a, b) + a.chunk - 1) / a.chunk;  // the splits the partial kernel wrote
+        M = lane < live ? mv : kNegInf;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = wo[(int64_t)min(j0 + u, n - 1) * D];
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float w = lane < live ? exp2f(mv - M) : 0.0f;
+        lsum = lane < live ? w * lv : 0.0f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(j0 + u, 63)));
-                o += j0 + u < n ? wj * v[u] : 0.0f;
+        for (int u = 0; u < kPre; ++u) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+            o += u < live ? wj * v[u] : 0.0f;
+        }
+    } else {
+        live = (seq_len(a, b) + a.chunk - 1) / a.chunk;
+        for (int s0 = 0; s0 < live; s0 += 64) M = fmaxf(M, s0 + lane < live ? a.ws_m[p0 + s0 + lane] : kNegInf);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        for (int s0 = 0; s0 < live; s0 += 64) {
+            const int s = s0 + lane;
+            const float w = s < live ? exp2f(a.ws_m[p0 + s] - M) : 0.0f;
+            lsum += s < live ? w * a.ws_l[p0 + s] : 0.0f;
+            const int n = min(64, live - s0);
+            const float* wo = a.ws_o + (p0 + s0) * D + d;
+            for (int j0 = 0; j0 < n; j0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = wo[(int64_t)min(j0 + u, n - 1) * D];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(j0 + u, 63)));
+                    o += j0 + u < n ? wj * v[u] : 0.0f;
+                }
             }
         }
     }
