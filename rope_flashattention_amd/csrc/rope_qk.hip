@@ -13,7 +13,9 @@
 // together with chunk j + D/2 (for the rotate-half pairing the two are partners; for the
 // interleaved pairing each chunk holds whole pairs).  It loads (or forms) the four table
 // chunks once and then walks a group of heads (q heads first, then k heads), so table
-// traffic is amortised over the group.
+// traffic is amortised over the group.  Calls that move more than twice the last-level
+// cache use nontemporal loads and stores (measured on B1 H64/8 S16384, 612 MB: 5.45 -> 5.8
+// TB/s; on the smaller workloads, whose output the cache still holds, they are slower).
 #include "common.h"
 
 namespace ropefa {
@@ -98,15 +100,50 @@ __device__ __forceinline__ void qk_table_values(const QkArgs& a, int64_t trow, i
     }
 }
 
-template <typename T, int PAIR, bool GEN>
+constexpr int kQkMaxHeads = 8;  // heads one thread rotates (heads_per_block <= this)
+// Calls that move more than this (q and k read and written) stream past the caches: twice
+// the 256 MB last-level cache, so nothing the call writes would still be there when read.
+constexpr uint64_t kQkStreamBytes = 512ull << 20;
+
+template <bool NT, typename T>
+__device__ __forceinline__ Chunk8<T> qk_load(const T* p) {
+    if constexpr (NT) return load_stream<T>(p);
+    else return load_chunk<T>(p);
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void qk_store(T* p, const Chunk8<T>& c) {
+    if constexpr (NT) store_stream<T>(p, c);
+    else store_chunk<T>(p, c);
+}
+
+// HEADS_INNER (layouts whose heads are contiguous within a token, BSND and packed TND):
+// one thread per (token, head, chunk), the chunk index fastest and then the head, so a
+// wave's loads cover whole head rows of one token; the table chunks, the same for all heads
+// of a token, are read by every head's lanes from the same addresses.  Otherwise (BNSD,
+// where a head's tokens are contiguous): one thread per (token, chunk), walking the
+// workgroup's group of heads.
+template <typename T, int PAIR, bool GEN, bool NT, bool HEADS_INNER>
 __global__ __launch_bounds__(256) void rope_qk_kernel(QkArgs a) {
     const int D = a.head_dim;
     const int half = D >> 1;
     const int chunks = half >> 3;
+    const int heads = a.hq + a.hkv;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)a.rows * chunks) return;
-    const int t = (int)(gid / chunks);
-    const int j = (int)(gid - (int64_t)t * chunks) * 8;
+    int t, j, h0, nh;
+    if constexpr (HEADS_INNER) {
+        if (gid >= (int64_t)a.rows * heads * chunks) return;
+        const int64_t th = gid / chunks;
+        j = (int)(gid - th * chunks) * 8;
+        t = (int)(th / heads);
+        h0 = (int)(th - (int64_t)t * heads);
+        nh = 1;
+    } else {
+        if (gid >= (int64_t)a.rows * chunks) return;
+        t = (int)(gid / chunks);
+        j = (int)(gid - (int64_t)t * chunks) * 8;
+        h0 = blockIdx.y * a.heads_per_block;
+        nh = min(a.heads_per_block, heads - h0);
+    }
 
     // token -> (sequence, position) offsets and table row
     int64_t qoff, koff, trow;
@@ -130,37 +167,89 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(QkArgs a) {
     float c0[8], s0[8], c1[8], s1[8];
     qk_table_values<T, PAIR, GEN>(a, trow, b, j, c0, s0, c1, s1);
 
-    const int h0 = blockIdx.y * a.heads_per_block;
-    const int h1 = min(h0 + a.heads_per_block, a.hq + a.hkv);
-    for (int hh = h0; hh < h1; ++hh) {
+    auto head_ptrs = [&](int hh, const T*& src, T*& dst) {
         const bool isq = hh < a.hq;
         const int h = isq ? hh : hh - a.hq;
-        const T* src = reinterpret_cast<const T*>(isq ? a.q : a.k) + (isq ? qoff + (int64_t)h * a.qs[2] : koff + (int64_t)h * a.ks[2]);
-        T* dst = reinterpret_cast<T*>(isq ? a.oq : a.ok) + (isq ? qoff + (int64_t)h * a.qs[2] : koff + (int64_t)h * a.ks[2]);
+        const int64_t off = isq ? qoff + (int64_t)h * a.qs[2] : koff + (int64_t)h * a.ks[2];
+        src = reinterpret_cast<const T*>(isq ? a.q : a.k) + off;
+        dst = reinterpret_cast<T*>(isq ? a.oq : a.ok) + off;
+    };
+    auto rotate_store = [&](const Chunk8<T>& xc, const Chunk8<T>& yc, T* dst) {
         float x[8], y[8];
-        unpack<T>(load_chunk<T>(src + j), x);
-        unpack<T>(load_chunk<T>(src + j + half), y);
+        unpack<T>(xc, x);
+        unpack<T>(yc, y);
         if (PAIR == ROPE_PAIR_HALF) {
             rotate_pair(x, y, c0, s0, c1, s1);
         } else {
             rotate_interleaved(x, c0, s0);
             rotate_interleaved(y, c1, s1);
         }
-        store_chunk<T>(dst + j, pack<T>(x));
-        store_chunk<T>(dst + j + half, pack<T>(y));
+        qk_store<NT, T>(dst + j, pack<T>(x));
+        qk_store<NT, T>(dst + j + half, pack<T>(y));
+    };
+    if constexpr (NT || HEADS_INNER) {
+        // streaming (data beyond the caches), or one head per thread: head by head
+        for (int i = 0; i < nh; ++i) {
+            const T* src;
+            T* dst;
+            head_ptrs(h0 + i, src, dst);
+            const Chunk8<T> xc = qk_load<NT, T>(src + j);
+            const Chunk8<T> yc = qk_load<NT, T>(src + j + half);
+            rotate_store(xc, yc, dst);
+        }
+    } else {
+        // every load of the thread's heads is issued before the first rotation and store, so
+        // a thread keeps 2 * kQkMaxHeads loads in flight instead of 2 (a store may alias the
+        // next head's load when the call is in place, which otherwise keeps each head's loads
+        // behind the previous head's stores)
+        Chunk8<T> xr[kQkMaxHeads], yr[kQkMaxHeads];
+#pragma unroll
+        for (int i = 0; i < kQkMaxHeads; ++i) {
+            if (i < nh) {
+                const T* src;
+                T* dst;
+                head_ptrs(h0 + i, src, dst);
+                xr[i] = qk_load<NT, T>(src + j);
+                yr[i] = qk_load<NT, T>(src + j + half);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kQkMaxHeads; ++i) {
+            if (i < nh) {
+                const T* src;
+                T* dst;
+                head_ptrs(h0 + i, src, dst);
+                rotate_store(xr[i], yr[i], dst);
+            }
+        }
+    }
+}
+
+template <typename T, bool NT, bool HI>
+static void launch_qk_mode(const QkArgs& a, int pairing, bool gen, dim3 grid, hipStream_t stream) {
+    const dim3 block(256);
+    const int key = pairing * 2 + (gen ? 1 : 0);
+    switch (key) {
+        case 0: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_HALF, false, NT, HI>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_HALF, true, NT, HI>), grid, block, 0, stream, a); break;
+        case 2:
+            hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_INTERLEAVED, false, NT, HI>), grid, block, 0, stream, a);
+            break;
+        case 3:
+            hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_INTERLEAVED, true, NT, HI>), grid, block, 0, stream, a);
+            break;
     }
 }
 
 template <typename T>
-static void launch_qk_typed(const QkArgs& a, int pairing, bool gen, dim3 grid, hipStream_t stream) {
-    const dim3 block(256);
-    const int key = pairing * 2 + (gen ? 1 : 0);
-    switch (key) {
-        case 0: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_HALF, false>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_HALF, true>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_INTERLEAVED, false>), grid, block, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((rope_qk_kernel<T, ROPE_PAIR_INTERLEAVED, true>), grid, block, 0, stream, a); break;
-    }
+static void launch_qk_typed(const QkArgs& a, int pairing, bool gen, bool nt, bool hi, dim3 grid,
+                            hipStream_t stream) {
+    if (nt)
+        hi ? launch_qk_mode<T, true, true>(a, pairing, gen, grid, stream)
+           : launch_qk_mode<T, true, false>(a, pairing, gen, grid, stream);
+    else
+        hi ? launch_qk_mode<T, false, true>(a, pairing, gen, grid, stream)
+           : launch_qk_mode<T, false, false>(a, pairing, gen, grid, stream);
 }
 
 hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
@@ -189,18 +278,30 @@ hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
     a.inv_freq_rows = p->inv_freq_rows;
     a.pos_scale = p->pos_scale;
     const bool gen = p->cos == nullptr;
-    // heads per block: enough blocks to fill the chip, table reuse across the group
     const int heads = p->hq + p->hkv;
-    const int64_t threads = (int64_t)a.rows * (p->head_dim / 16);
-    const int64_t blocks_x = (threads + 255) / 256;
-    int hpb = 8;
-    while (hpb > 1 && blocks_x * ((heads + hpb - 1) / hpb) < 2048) hpb >>= 1;
-    a.heads_per_block = hpb;
-    const dim3 grid((unsigned)blocks_x, (unsigned)((heads + hpb - 1) / hpb));
+    const int chunks = p->head_dim / 16;
+    // heads contiguous within a token (BSND, packed TND): one thread per (token, head, chunk)
+    const bool hi = p->q_stride[2] < p->q_stride[1] && p->k_stride[2] < p->k_stride[1] &&
+                    ((int64_t)a.rows * heads * chunks + 255) / 256 <= (int64_t)INT32_MAX;
+    dim3 grid;
+    if (hi) {
+        a.heads_per_block = 1;
+        grid = dim3((unsigned)(((int64_t)a.rows * heads * chunks + 255) / 256));
+    } else {
+        // heads per block: enough blocks to fill the chip, table reuse across the group
+        const int64_t blocks_x = ((int64_t)a.rows * chunks + 255) / 256;
+        int hpb = kQkMaxHeads;
+        while (hpb > 1 && blocks_x * ((heads + hpb - 1) / hpb) < 2048) hpb >>= 1;
+        a.heads_per_block = hpb;
+        grid = dim3((unsigned)blocks_x, (unsigned)((heads + hpb - 1) / hpb));
+    }
+    const uint64_t moved = 2ull * (uint64_t)a.rows * (uint64_t)heads * (uint64_t)p->head_dim *
+                           (uint64_t)dtype_bytes(p->dtype);
+    const bool nt = moved > kQkStreamBytes;
     switch (p->dtype) {
-        case ROPE_DT_BF16: launch_qk_typed<__bf16>(a, p->pairing, gen, grid, stream); break;
-        case ROPE_DT_F16: launch_qk_typed<_Float16>(a, p->pairing, gen, grid, stream); break;
-        case ROPE_DT_F32: launch_qk_typed<float>(a, p->pairing, gen, grid, stream); break;
+        case ROPE_DT_BF16: launch_qk_typed<__bf16>(a, p->pairing, gen, nt, hi, grid, stream); break;
+        case ROPE_DT_F16: launch_qk_typed<_Float16>(a, p->pairing, gen, nt, hi, grid, stream); break;
+        case ROPE_DT_F32: launch_qk_typed<float>(a, p->pairing, gen, nt, hi, grid, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -182,6 +182,24 @@ def test_rope_qk_bsnd_and_in_place():
     assert torch.equal(q2, oq) and torch.equal(k2, ok)
 
 
+@pytest.mark.parametrize("case", ["bsnd", "varlen", "long_streaming"])
+def test_rope_qk_in_place_every_thread_mapping(case):
+    """In place equals out of place on each of rope_qk's paths: heads inner (BSND, packed
+    TND), and the streaming path of calls larger than twice the last-level cache (the long
+    GQA workload at full size, 612 MB)."""
+    w = {"bsnd": wl.SMALL[2], "varlen": wl.SMALL[4], "long_streaming": wl.CONFIGS[5]}[case]
+    inp = wl.generate(w)
+    dev = device()
+    lay = "TND" if w.varlen else ("BSND" if case == "bsnd" else "BNSD")
+    q, k, _ = to_dev(inp, lay)
+    s, c, tsr = gpu_tables(inp, shared=False)
+    kw = dict(layout="TND", cu_seqlens=torch.from_numpy(wl.cu_seqlens(inp.seq_lens)).to(dev),
+              max_seqlen=int(inp.seq_lens.max())) if w.varlen else dict(layout=lay)
+    oq, ok = rfa.rope_qk(q, k, c, s, table_seq_rows=tsr, **kw)
+    rfa.rope_qk(q, k, c, s, table_seq_rows=tsr, out_q=q, out_k=k, **kw)
+    assert torch.equal(q, oq) and torch.equal(k, ok)
+
+
 # --------------------------------------------------------------------------- attention, full output
 def _attn_check(inp, layout="BNSD", shared_table=True):
     w = inp.workload
