@@ -415,7 +415,7 @@ def main():
             # head_size 2048 (2.1 GB written) and 512
             lens = np.full(16, 16000, dtype=np.int32)
             tpos = torch.arange(16000, dtype=torch.int32, device=dev).repeat(16)
-            for Dt in (2048, 512):
+            for Dt in (2048, 512, 128):
                 tf = torch.from_numpy(rfa.inv_freq(1e4, Dt, lens, 4096)).to(dev)
                 variants = []
                 for dt_name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
