@@ -22,13 +22,16 @@
 //     rescale by exp2(m_old - m_new)) moves only on the first tile or when a row sum of
 //     the tile exceeds 2^16, i.e. when some score has outgrown the reference; then the
 //     tile's row max is taken and P recomputed.  P stays below 2^16 otherwise, far inside
-//     the float32/bf16 range.  Row sums add the rounded P with v_dot2 (exactly the values
-//     the PV product uses).
+//     the float32/bf16 range.  Row sums add the float32 exponentials.
 //   * O^T += V^T P^T with the same MFMA: P is already in the B-operand layout, and the
 //     V^T operand comes from row-major V in LDS through the transposing LDS read
 //     (ds_read_b64_tr_b16).
 //   * Meanwhile the next tile, loaded into registers one tile ahead, is rotated (K) and
-//     written to the other LDS buffer; the loads for the tile after it are issued.
+//     written to the other LDS buffer; the loads for the tile after it are issued.  For
+//     rotate-half tables at head_dim 128 the rotation is cut into 16 slices, one after each
+//     P.V MFMA (the four O blocks in turn, operands read three steps ahead), so the vector
+//     work issues while the matrix core runs.  No v_dot2 anywhere: on gfx950 those run in
+//     the matrix-core pipeline and would serialise with the MFMAs.
 // Permuted K' rows: MFMA result row m of S^T is key pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3)
 // inside a 32-key block, which makes the 16 scores of lane half h the contiguous keys
 // 16h .. 16h+15; K' for key pi(m) is stored at LDS row m so the MFMA reads consecutive rows.
@@ -104,14 +107,12 @@ __device__ __forceinline__ void gen_table_chunk_inter(int32_t p, float pos_scale
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
     typedef bf16x8 vec;
-    static constexpr uint32_t ones = 0x3f803f80u;  // (1, 1) in bf16
     __device__ static __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
 };
 template <> struct Mfma<_Float16> {
     typedef f16x8 vec;
-    static constexpr uint32_t ones = 0x3c003c00u;  // (1, 1) in fp16
     __device__ static __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             }
             // ---- P = exp2(S - m) rounded to T, and this lane's part of the tile row sum
             auto exp_pack = [&]() {
-                float lt = 0.f;
+                float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -468,13 +469,14 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                         u32x4 pw;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            pw[e] = Elem<T>::pack(__builtin_amdgcn_exp2f(sacc[blk][8 * s + 2 * e]),
-                                                  __builtin_amdgcn_exp2f(sacc[blk][8 * s + 2 * e + 1]));
-                            lt = Elem<T>::dot2(pw[e], Mfma<T>::ones, lt);
+                            const float e0 = __builtin_amdgcn_exp2f(sacc[blk][8 * s + 2 * e]);
+                            const float e1 = __builtin_amdgcn_exp2f(sacc[blk][8 * s + 2 * e + 1]);
+                            pw[e] = Elem<T>::pack(e0, e1);
+                            lsum[e] += e0 + e1;
                         }
                         pk[blk][s] = __builtin_bit_cast(vec, pw);
                     }
-                return lt;
+                return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
             };
             const bool first = m_run == -INFINITY;
             float lt = 0.f;
@@ -509,6 +511,66 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             l_run += lt;
         }
 
+        constexpr bool kSliced = ROT == kRotHalfTable && NKI == 1 && KITEMS == NT && D == 128;
+        if constexpr (kSliced) {
+            // ---- O^T += V^T P^T, each MFMA followed by a slice of the next tile's K rotation
+            // (vector work the matrix core does not wait for); the P.V of inactive waves
+            // multiplies P = 0 (set below) so that every wave runs the same straight block
+            if (!active) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) pk[i][j] = __builtin_bit_cast(vec, u32x4{0u, 0u, 0u, 0u});
+            }
+            const T* vp0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
+            auto rd_v = [&](int j) {
+                const T* vp = vp0 + ((j >> 3) * 32 + 8 * ((j >> 2) & 1)) * VP + (j & 3) * 32;
+                const i16x4 lo = lds_read_tr16(vp);
+                const i16x4 hi = lds_read_tr16(vp + 4 * VP);
+                return __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            float rx0 = 0.f, rx1 = 0.f, ry0 = 0.f, ry1 = 0.f, rc0 = 0.f, rc1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+            u32x4 kxo, kyo;
+            auto rot_slice = [&](int sl) {
+                const int i = sl >> 2, q = sl & 3;
+                if (q == 0) {
+                    rx0 = Elem<T>::lo(kx[0][i]); rx1 = Elem<T>::hi(kx[0][i]);
+                    ry0 = Elem<T>::lo(ky[0][i]); ry1 = Elem<T>::hi(ky[0][i]);
+                } else if (q == 1) {
+                    rc0 = Elem<T>::lo(kc[0][i]); rc1 = Elem<T>::hi(kc[0][i]);
+                    rs0 = Elem<T>::lo(ks[0][i]); rs1 = Elem<T>::hi(ks[0][i]);
+                } else if (q == 2) {
+                    kxo[i] = Elem<T>::pack(__builtin_fmaf(rx0, rc0, -(ry0 * rs0)), __builtin_fmaf(rx1, rc1, -(ry1 * rs1)));
+                } else {
+                    kyo[i] = Elem<T>::pack(__builtin_fmaf(ry0, rc0, rx0 * rs0), __builtin_fmaf(ry1, rc1, rx1 * rs1));
+                }
+            };
+            constexpr int PD = 3;
+            vec vb[PD + 1];
+#pragma unroll
+            for (int j = 0; j < PD; ++j) vb[j] = rd_v(j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j + PD < 16) vb[(j + PD) % (PD + 1)] = rd_v(j + PD);
+                oacc[j & 3] = Mfma<T>::run(vb[j % (PD + 1)], pk[j >> 3][(j >> 2) & 1], oacc[j & 3]);
+                rot_slice(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the staged tile's stores (into the other buffers) and the loads of the one after
+            {
+                T* dst = &sK[buf ^ 1][kprime_row(tid / KCH) * KP + (tid % KCH) * 8];
+                *reinterpret_cast<u32x4*>(dst) = kxo;
+                *reinterpret_cast<u32x4*>(dst + HALF) = kyo;
+#pragma unroll
+                for (int j = 0; j < NVI; ++j) {
+                    const int it = tid + j * NT;
+                    const int kap = it / (D / 8), c = (it % (D / 8)) * 8;
+                    *reinterpret_cast<u32x4*>(&sV[buf ^ 1][kap * VP + c]) = vr[j];
+                }
+            }
+            if (kt + 2 < n_kt) stage_load(kt + 2);
+        } else {
         // ---- stage the next tile (rotate K) into the other buffer, prefetch the one after
         if (kt + 1 < n_kt) stage_store(buf ^ 1);
         if (kt + 2 < n_kt) stage_load(kt + 2);
@@ -527,6 +589,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                         const vec av = __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         oacc[mb] = Mfma<T>::run(av, pk[blk][s], oacc[mb]);
                     }
+        }
         }
         __syncthreads();
     }
