@@ -540,9 +540,11 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                     rc0 = Elem<T>::lo(kc[0][i]); rc1 = Elem<T>::hi(kc[0][i]);
                     rs0 = Elem<T>::lo(ks[0][i]); rs1 = Elem<T>::hi(ks[0][i]);
                 } else if (q == 2) {
-                    kxo[i] = Elem<T>::pack(__builtin_fmaf(rx0, rc0, -(ry0 * rs0)), __builtin_fmaf(rx1, rc1, -(ry1 * rs1)));
+                    kxo[i] = Elem<T>::pack(__builtin_fmaf(rx0, rc0, -__fmul_rn(ry0, rs0)),
+                                           __builtin_fmaf(rx1, rc1, -__fmul_rn(ry1, rs1)));
                 } else {
-                    kyo[i] = Elem<T>::pack(__builtin_fmaf(ry0, rc0, rx0 * rs0), __builtin_fmaf(ry1, rc1, rx1 * rs1));
+                    kyo[i] = Elem<T>::pack(__builtin_fmaf(ry0, rc0, __fmul_rn(rx0, rs0)),
+                                           __builtin_fmaf(ry1, rc1, __fmul_rn(rx1, rs1)));
                 }
             };
             constexpr int PD = 3;
