@@ -26,9 +26,11 @@
 //     dQ'^T += K'^T dS^T (K'^T by the transposing read).
 // An LDS tile read both ways is stored twice: rows in the pi order for the row reads and
 // in natural order for the transposing reads, each at a padded pitch (bank-conflict free
-// reads, constant read offsets).  Each kernel loads the next block into registers while
-// it computes the current one (LDS double-buffered, one barrier per block); the
-// workgroups that read the same rows run on one XCD in step.  The epilogues apply M^T
+// reads, constant read offsets).  Each kernel loads its blocks two ahead into two register
+// sets used in turn (a block's loads then have a whole block's compute to arrive), LDS is
+// double-buffered with one barrier per block, and the A operands of the row reads are
+// fetched two products ahead; the workgroups that read the same rows run on one XCD in
+// step.  The epilogues apply M^T
 // (the transposed Rope op) to dq' and dk' before the stores.
 #include <type_traits>
 
@@ -245,7 +247,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 template <typename T, int D, int PAIR>
 __device__ __forceinline__ void store_grad_row(const f32x16 (&acc)[D / 32], float scale, int hh, const T* crow,
                                                const T* srow, T* dst) {
-    constexpr int HALF = D / 2;
     float g[D / 32][16];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -374,29 +375,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int sr = (tid % QITEMS) / CPR, sc = (tid % CPR) * 8;
     // Every thread issues its loads unconditionally (no branch around a load, so no wait
     // is forced at a join); the loaded values are only used at the next block's store.
-    StageItem pre;
-    float pre_l, pre_d;  // raw lse and delta of row (tid & 31) of the block
-    auto load_block = [&](int hi, int q0) {
+    StageItem pre[2];
+    float pre_l[2], pre_d[2];  // raw lse and delta of row (tid & 31) of the block
+    auto load_block = [&](auto slot, int hi, int q0) {
+        constexpr int S = decltype(slot)::value;
         const int h = kvh * a.group + hi;
         const int qi = min(q0 + sr, L - 1);
-        stage_load<T>(pre, Qr + ((int64_t)h * a.rows + qi) * D, Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], sc,
+        stage_load<T>(pre[S], Qr + ((int64_t)h * a.rows + qi) * D, Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], sc,
                       HALF);
         const int64_t idx = (int64_t)h * a.lse_stride + sq.tok + min(q0 + (tid & 31), L - 1);
-        pre_l = a.lse[idx];
-        pre_d = a.delta[idx];
+        pre_l[S] = a.lse[idx];
+        pre_d[S] = a.delta[idx];
     };
-    auto store_block = [&](int buf, int q0) {
+    auto store_block = [&](auto slot, int buf, int q0) {
+        constexpr int S = decltype(slot)::value;
         if (stager) {
-            store_rowcopy<T, D>(sQa[buf], sr, sc, pre.a0, pre.a1);
-            store_trcopy<T, D>(sQt[buf], sr, sc, pre.a0, pre.a1);
-            store_rowcopy<T, D>(sDa[buf], sr, sc, pre.b0, pre.b1);
-            store_trcopy<T, D>(sDt[buf], sr, sc, pre.b0, pre.b1);
+            store_rowcopy<T, D>(sQa[buf], sr, sc, pre[S].a0, pre[S].a1);
+            store_trcopy<T, D>(sQt[buf], sr, sc, pre[S].a0, pre[S].a1);
+            store_rowcopy<T, D>(sDa[buf], sr, sc, pre[S].b0, pre[S].b1);
+            store_trcopy<T, D>(sDt[buf], sr, sc, pre[S].b0, pre[S].b1);
         }
         if (tid < 32) {
             // rows past the end get lse = +inf: their P is exactly 0
             const bool ok = q0 + tid < L;
-            sL[buf][tid] = ok ? pre_l * kLog2e : __builtin_inff();
-            sDel[buf][tid] = ok ? pre_d : 0.0f;
+            sL[buf][tid] = ok ? pre_l[S] * kLog2e : __builtin_inff();
+            sDel[buf][tid] = ok ? pre_d[S] : 0.0f;
         }
     };
 
@@ -431,42 +434,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     // within each; the workgroups of all key tiles of this (sequence, kv head) start
     // together at the last block and stay in step, reading the same rows at the same time
     const int q_last = q_begin + ((L - 1 - q_begin) >> 5) * 32;
-    int ld_hi = 0, ld_q0 = q_last;
-    load_block(ld_hi, ld_q0);
-    for (int buf = 0;; buf ^= 1) {
-        const int q0 = ld_q0;
-        store_block(buf, q0);
-        __syncthreads();  // block visible; every read of this buffer two blocks back is done
+    // Block loads run two blocks ahead, into two register sets used in turn: block j is
+    // stored from its set at iteration j, which then receives block j + 2.
+    int ld_hi = 0, ld_q0 = q_last;  // next block to load
+    auto advance = [&]() {
         if (++ld_hi == a.group) {
             ld_hi = 0;
             ld_q0 -= 32;
         }
-        const bool more = ld_q0 >= q_begin;
-        // after the last block this reloads a valid one (never stored): no branch
-        load_block(more ? ld_hi : 0, more ? ld_q0 : q_begin);
+    };
+    auto load_next = [&](auto slot) {
+        const bool ok = ld_q0 >= q_begin;
+        load_block(slot, ok ? ld_hi : 0, ok ? ld_q0 : q_begin);  // past the end: a valid dummy, never stored
+        const int q = ld_q0;
+        advance();
+        return q;
+    };
+    int cq0 = load_next(std::integral_constant<int, 0>{});  // block j
+    int nq0 = load_next(std::integral_constant<int, 1>{});  // block j + 1 (below q_begin: none)
+    int buf = 0;
+    auto iter = [&](auto slot) {
+        const int q0 = cq0;
+        store_block(slot, buf, q0);
+        __syncthreads();  // block visible; every read of this buffer two blocks back is done
+        cq0 = nq0;
+        nq0 = load_next(slot);
         if (active && !(a.causal && q0 + 31 < kw0)) {  // wave-uniform
             const T* qa = sQa[buf];
             const T* qt = sQt[buf];
             const T* da = sDa[buf];
             const T* dt = sDt[buf];
             // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i
-            // every A operand is read before the first product, so the products do not wait
-            // on one LDS round trip each
-            u32x4 aq[NS], ad[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
+            // A operands read two products ahead (a ring of three), so the products do not
+            // wait on one LDS round trip each
+            constexpr int PD = 2;
+            u32x4 aq[PD + 1], ad[PD + 1];
+            auto rd_a = [&](int s) {
                 const int off = n * PA + 16 * s + 8 * hh;
-                aq[s] = *reinterpret_cast<const u32x4*>(&qa[off]);
-                ad[s] = *reinterpret_cast<const u32x4*>(&da[off]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                aq[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&qa[off]);
+                ad[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&da[off]);
+            };
+#pragma unroll
+            for (int s = 0; s < PD; ++s) rd_a(s);
             f32x16 sacc, dpacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                sacc = BMma<T>::run(aq[s], kb[s], sacc);
-                dpacc = BMma<T>::run(ad[s], vb[s], dpacc);
+                if (s + PD < NS) rd_a(s + PD);
+                sacc = BMma<T>::run(aq[s % (PD + 1)], kb[s], sacc);
+                dpacc = BMma<T>::run(ad[s % (PD + 1)], vb[s], dpacc);
+                __builtin_amdgcn_sched_barrier(0);
             }
             const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
             float lv[16], dl[16];
@@ -522,7 +541,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
                                              dsk[s], dkacc[mb]);
                 }
         }
-        if (!more) break;
+        buf ^= 1;
+        return cq0 >= q_begin;
+    };
+    for (;;) {
+        if (!iter(std::integral_constant<int, 0>{})) break;
+        if (!iter(std::integral_constant<int, 1>{})) break;
     }
 
     // ---- epilogue: dk = M^T (s * dK'), dv as accumulated
@@ -578,25 +602,27 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 
     // ---- staging: NKI items per thread of each key tile; rows past the end re-read the
     // last row (finite, masked below)
-    StageItem pre[NKI];
-    auto load_tile = [&](int k0) {
+    StageItem pre[2][NKI];  // two register sets: tile loads run two tiles ahead
+    auto load_tile = [&](auto slot, int k0) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < NKI; ++j) {
             const int it = (tid + j * NT) % KITEMS;  // spare threads load a duplicate, never stored
             const int r = it / CPR, c = (it % CPR) * 8;
             const int kr = min(k0 + r, L - 1);
-            stage_load<T>(pre[j], Kr + (int64_t)kr * D, Vg + (int64_t)kr * a.vs[1], c, HALF);
+            stage_load<T>(pre[S][j], Kr + (int64_t)kr * D, Vg + (int64_t)kr * a.vs[1], c, HALF);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](auto slot, int buf) {
+        constexpr int S = decltype(slot)::value;
 #pragma unroll
         for (int j = 0; j < NKI; ++j) {
             const int it = tid + j * NT;
             if (KITEMS % NT == 0 || it < KITEMS) {
                 const int r = it / CPR, c = (it % CPR) * 8;
-                store_rowcopy<T, D>(sKa[buf], r, c, pre[j].a0, pre[j].a1);
-                store_trcopy<T, D>(sKt[buf], r, c, pre[j].a0, pre[j].a1);
-                store_rowcopy<T, D>(sVa[buf], r, c, pre[j].b0, pre[j].b1);
+                store_rowcopy<T, D>(sKa[buf], r, c, pre[S][j].a0, pre[S][j].a1);
+                store_trcopy<T, D>(sKt[buf], r, c, pre[S][j].a0, pre[S][j].a1);
+                store_rowcopy<T, D>(sVa[buf], r, c, pre[S][j].b0, pre[S][j].b1);
             }
         }
     };
@@ -634,14 +660,18 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     // key kk of this lane's row is kept iff kk <= kmax
     const int kmax = a.causal ? min(qi, L - 1) : L - 1;
 
-    load_tile(0);
-    for (int kt = 0, buf = 0; kt < n_kt; ++kt, buf ^= 1) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_tile(S0{}, 0);
+    load_tile(S1{}, min(KT, (n_kt - 1) * KT));
+    auto iter = [&](auto slot, int kt) {
         const int k0 = kt * KT;
-        store_tile(buf);
+        const int buf = kt & 1;
+        store_tile(slot, buf);
         __syncthreads();  // tile visible; every read of this buffer two tiles back is done
-        // after the last tile this reloads it (never stored): no branch around the loads
-        load_tile(min(k0 + KT, (n_kt - 1) * KT));
-        if (!active || k0 >= wave_kend) continue;  // wave-uniform
+        // near the end this reloads the last tile (never stored): no branch around the loads
+        load_tile(slot, min(k0 + 2 * KT, (n_kt - 1) * KT));
+        if (!active || k0 >= wave_kend) return;  // wave-uniform
         const T* ka = sKa[buf];
         const T* ktr = sKt[buf];
         const T* va = sVa[buf];
@@ -693,6 +723,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                                              dsk[s], dqacc[mb]);
                 }
         }
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        iter(S0{}, kt);
+        if (kt + 1 < n_kt) iter(S1{}, kt + 1);
     }
 
     // ---- epilogue: dq = M^T (s * dQ')

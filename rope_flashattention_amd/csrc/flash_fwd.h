@@ -12,8 +12,9 @@
 // query tiles, sequences); query tiles are issued longest-first for causal balance.
 //
 // Per key tile of 64 keys (LDS double-buffered, one barrier per tile):
-//   * S^T = K' Q'^T with 32x32x16 MFMA: A = K' rows from LDS, B = Q' held in registers
-//     since the start (rotated and multiplied by softmax_scale*log2(e) once).  A lane
+//   * S^T = K' Q'^T with 32x32x16 MFMA: A = K' rows from LDS (read four products ahead),
+//     B = Q' held in registers since the start (rotated and multiplied by
+//     softmax_scale*log2(e) once).  A lane
 //     therefore holds 16 scores of one query row and the row statistics need a single
 //     exchange between the two halves of the wave (v_permlane32_swap).
 //   * Online softmax in the log2 domain with a lazily updated reference m: the MFMA
@@ -437,16 +438,20 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             // ---- S^T - m = K' Q'^T - m : lane (r, h) gets keys k0 + 32*blk + 16h + i of query qi
             f32x16 sacc[2];
             {
+                // the 2*(D/16) K' operands (block j & 1, column step j >> 1) are read four
+                // products ahead, so the MFMAs do not wait on one LDS round trip each
                 const T* kp0 = &sK[buf][r * KP + 8 * h];
-                const T* kp1 = kp0 + 32 * KP;
-                sacc[0] = Mfma<T>::run(*reinterpret_cast<const vec*>(kp0), qreg[0], minit);
-                sacc[1] = Mfma<T>::run(*reinterpret_cast<const vec*>(kp1), qreg[0], minit);
+                auto rd_k = [&](int j) { return *reinterpret_cast<const vec*>(kp0 + (j & 1) * 32 * KP + 16 * (j >> 1)); };
+                constexpr int NS = 2 * (D / 16), SPD = 4;
+                vec kb[SPD + 1];
 #pragma unroll
-                for (int u = 1; u < D / 16; ++u) {
-                    const vec kv0 = *reinterpret_cast<const vec*>(kp0 + 16 * u);
-                    const vec kv1 = *reinterpret_cast<const vec*>(kp1 + 16 * u);
-                    sacc[0] = Mfma<T>::run(kv0, qreg[u], sacc[0]);
-                    sacc[1] = Mfma<T>::run(kv1, qreg[u], sacc[1]);
+                for (int j = 0; j < SPD; ++j) kb[j] = rd_k(j);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    if (j + SPD < NS) kb[(j + SPD) % (SPD + 1)] = rd_k(j + SPD);
+                    sacc[j & 1] = Mfma<T>::run(kb[j % (SPD + 1)], qreg[j >> 1], j < 2 ? minit : sacc[j & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // ---- masks: causal (key > query) and the ragged end of the sequence: key
