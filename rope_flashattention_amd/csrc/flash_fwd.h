@@ -29,10 +29,10 @@
 //     (ds_read_b64_tr_b16).
 //   * Meanwhile the next tile, loaded into registers one tile ahead, is rotated (K) and
 //     written to the other LDS buffer; the loads for the tile after it are issued.  For
-//     rotate-half tables at head_dim 128 the rotation is cut into 16 slices, one after each
-//     P.V MFMA (the four O blocks in turn, operands read three steps ahead), so the vector
-//     work issues while the matrix core runs.  No v_dot2 anywhere: on gfx950 those run in
-//     the matrix-core pipeline and would serialise with the MFMAs.
+//     tables read from memory (either pairing) at head_dim 128 the rotation is cut into 16
+//     slices, one after each P.V MFMA (the four O blocks in turn, operands read three steps
+//     ahead), so the vector work issues while the matrix core runs.  No v_dot2 anywhere: on
+//     gfx950 those run in the matrix-core pipeline and would serialise with the MFMAs.
 // Permuted K' rows: MFMA result row m of S^T is key pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3)
 // inside a 32-key block, which makes the 16 scores of lane half h the contiguous keys
 // 16h .. 16h+15; K' for key pi(m) is stored at LDS row m so the MFMA reads consecutive rows.
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             l_run += lt;
         }
 
-        constexpr bool kSliced = ROT == kRotHalfTable && NKI == 1 && KITEMS == NT && D == 128;
+        constexpr bool kSliced = (ROT == kRotHalfTable || ROT == kRotInterTable) && NKI == 1 && KITEMS == NT && D == 128;
         if constexpr (kSliced) {
             // ---- O^T += V^T P^T, each MFMA followed by a slice of the next tile's K rotation
             // (vector work the matrix core does not wait for); the P.V of inactive waves
@@ -537,6 +537,23 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             float rx0 = 0.f, rx1 = 0.f, ry0 = 0.f, ry1 = 0.f, rc0 = 0.f, rc1 = 0.f, rs0 = 0.f, rs1 = 0.f;
             u32x4 kxo, kyo;
             auto rot_slice = [&](int sl) {
+                if constexpr (ROT == kRotInterTable) {
+                    // word w of the x half (w < 4) or of the y half: unpack, then rotate and pack
+                    const int w = sl >> 1;
+                    const u32x4& src = w < 4 ? kx[0] : ky[0];
+                    const u32x4& tc = w < 4 ? kc[0] : kc2[0];
+                    const u32x4& ts = w < 4 ? ks[0] : ks2[0];
+                    if ((sl & 1) == 0) {
+                        rx0 = Elem<T>::lo(src[w & 3]); rx1 = Elem<T>::hi(src[w & 3]);
+                        rc0 = Elem<T>::lo(tc[w & 3]); rc1 = Elem<T>::hi(tc[w & 3]);
+                        rs0 = Elem<T>::lo(ts[w & 3]); rs1 = Elem<T>::hi(ts[w & 3]);
+                    } else {
+                        const uint32_t o = Elem<T>::pack(__builtin_fmaf(rx0, rc0, -__fmul_rn(rx1, rs0)),
+                                                         __builtin_fmaf(rx1, rc1, __fmul_rn(rx0, rs1)));
+                        if (w < 4) kxo[w] = o; else kyo[w & 3] = o;
+                    }
+                    return;
+                }
                 const int i = sl >> 2, q = sl & 3;
                 if (q == 0) {
                     rx0 = Elem<T>::lo(kx[0][i]); rx1 = Elem<T>::hi(kx[0][i]);
@@ -583,19 +600,28 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
         if (kt + 2 < n_kt) stage_load(kt + 2);
 
         if (active) {
-            // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T: product j updates O block j % NMB with key step j / NMB
+            // (the D/32 accumulator chains interleaved), operands read three products ahead
+            constexpr int NMB = D / 32, NJ = 4 * NMB, PD = 3;
+            const T* vp0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
+            auto rd_v = [&](int j) {
+                const int ks = j / NMB;
+                const T* vp = vp0 + ((ks >> 1) * 32 + 8 * (ks & 1)) * VP + (j % NMB) * 32;
+                const i16x4 lo = lds_read_tr16(vp);
+                const i16x4 hi = lds_read_tr16(vp + 4 * VP);
+                return __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            vec vb[PD + 1];
 #pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
+            for (int j = 0; j < PD; ++j) vb[j] = rd_v(j);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const T* vp = &sV[buf][(blk * 32 + 16 * h + 8 * s + tr_row) * VP + mb * 32 + tr_col];
-                        const i16x4 lo = lds_read_tr16(vp);
-                        const i16x4 hi = lds_read_tr16(vp + 4 * VP);
-                        const vec av = __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[mb] = Mfma<T>::run(av, pk[blk][s], oacc[mb]);
-                    }
+            for (int j = 0; j < NJ; ++j) {
+                if (j + PD < NJ) vb[(j + PD) % (PD + 1)] = rd_v(j + PD);
+                const int ks = j / NMB;
+                oacc[j % NMB] = Mfma<T>::run(vb[j % (PD + 1)], pk[ks >> 1][ks & 1], oacc[j % NMB]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         }
         __syncthreads();
