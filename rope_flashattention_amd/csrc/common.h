@@ -212,22 +212,25 @@ constexpr float kFastPathMax = 1048576.0f;  // 2^20
 // Taylor series truncated after r^11 and r^12 (remainders below 3e-9 relative), in
 // Horner form; the quadrant k mod 4 selects and signs the two results.  Larger
 // arguments use the device library's sincosf.
-__device__ __forceinline__ void rope_sincos(float x, float& s, float& c) {
-    if (__builtin_fabsf(x) > kFastPathMax) {
-        sincosf(x, &s, &c);
-        return;
-    }
-    const float k = __builtin_rintf(x * kTwoOverPi);
+//
+// The fast path comes in two halves, so that a caller can spread the work of several angles:
+// rope_sincos_a reduces the argument and evaluates the sine series, rope_sincos_b the
+// cosine series and the quadrant selection.  Run one after the other they are the fast
+// path of rope_sincos exactly.
+__device__ __forceinline__ void rope_sincos_a(float x, float& k, float& r2, float& sr) {
+    k = __builtin_rintf(x * kTwoOverPi);
     float r = __builtin_fmaf(-k, kHalfPiHi, x);
     r = __builtin_fmaf(-k, kHalfPiMid, r);
     r = __builtin_fmaf(-k, kHalfPiLo, r);
-    const float r2 = r * r;
+    r2 = r * r;
     // sin r = r + r^3 * (-1/3! + r^2 (1/5! + r^2 (-1/7! + r^2 (1/9! - r^2/11!))))
     float ps = __builtin_fmaf(r2, -1.0f / 39916800.0f, 1.0f / 362880.0f);
     ps = __builtin_fmaf(r2, ps, -1.0f / 5040.0f);
     ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
     ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
-    const float sr = __builtin_fmaf(r * r2, ps, r);
+    sr = __builtin_fmaf(r * r2, ps, r);
+}
+__device__ __forceinline__ void rope_sincos_b(float k, float r2, float sr, float& s, float& c) {
     // cos r = 1 + r^2 * (-1/2! + r^2 (1/4! + r^2 (-1/6! + r^2 (1/8! + r^2 (-1/10! + r^2/12!)))))
     float pc = __builtin_fmaf(r2, 1.0f / 479001600.0f, -1.0f / 3628800.0f);
     pc = __builtin_fmaf(r2, pc, 1.0f / 40320.0f);
@@ -241,6 +244,15 @@ __device__ __forceinline__ void rope_sincos(float x, float& s, float& c) {
     const float b = (q & 1) ? sr : cr;
     s = (q & 2) ? -a : a;
     c = ((q + 1) & 2) ? -b : b;
+}
+__device__ __forceinline__ void rope_sincos(float x, float& s, float& c) {
+    if (__builtin_fabsf(x) > kFastPathMax) {
+        sincosf(x, &s, &c);
+        return;
+    }
+    float k, r2, sr;
+    rope_sincos_a(x, k, r2, sr);
+    rope_sincos_b(k, r2, sr, s, c);
 }
 
 // The angle of one table entry in float32: fl32(fl32(pos / pos_scale) * inv_freq), each

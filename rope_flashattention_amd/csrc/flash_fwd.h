@@ -28,11 +28,13 @@
 //     V^T operand comes from row-major V in LDS through the transposing LDS read
 //     (ds_read_b64_tr_b16).
 //   * Meanwhile the next tile, loaded into registers one tile ahead, is rotated (K) and
-//     written to the other LDS buffer; the loads for the tile after it are issued.  For
-//     tables read from memory (either pairing) at head_dim 128 the rotation is cut into 16
-//     slices, one after each P.V MFMA (the four O blocks in turn, operands read three steps
-//     ahead), so the vector work issues while the matrix core runs.  No v_dot2 anywhere: on
-//     gfx950 those run in the matrix-core pipeline and would serialise with the MFMAs.
+//     written to the other LDS buffer; the loads for the tile after it are issued.  At
+//     head_dim 128 the rotation is cut into 16 slices, one after each P.V MFMA (the four O
+//     blocks in turn, operands read three steps ahead), so the vector work issues while
+//     the matrix core runs; with tables formed in the kernel the sine and cosine of the
+//     staged tile's columns are likewise computed in pieces between the score MFMAs.  No
+//     v_dot2 anywhere: on gfx950 those run in the matrix-core pipeline and would serialise
+//     with the MFMAs.
 // Permuted K' rows: MFMA result row m of S^T is key pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3)
 // inside a 32-key block, which makes the 16 scores of lane half h the contiguous keys
 // 16h .. 16h+15; K' for key pi(m) is stored at LDS row m so the MFMA reads consecutive rows.
@@ -183,6 +185,9 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     constexpr int NKI = (KITEMS + NT - 1) / NT;
     constexpr int NVI = (VITEMS + NT - 1) / NT;
     constexpr float kLazySum = 65536.0f;          // tile row sum that forces the reference to move
+    // formed tables at head_dim 128: the staged tile's sin/cos are computed between the score
+    // MFMAs and its rotation between the P.V MFMAs
+    constexpr bool kGenSliced = rot_gen(ROT) && NKI == 1 && KITEMS == NT && D == 128;
     typedef typename Mfma<T>::vec vec;
 
     __shared__ __attribute__((aligned(16))) T sK[2][kBN * KP];
@@ -434,6 +439,48 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
         const int k0 = kt * kBN;
         const bool active = k0 < wave_kend;  // wave-uniform: does this wave need any key here
         vec pk[2][2];
+        // formed tables: the staged tile's 8 table columns, each angle's sine half and cosine
+        // half one piece after each score MFMA, packed into the table registers in pairs
+        float gq = 0.f, gk = 0.f, gr2 = 0.f, gsr = 0.f, gcv[8], gsv[8];
+        bool gfar = false;
+        auto gen_finish = [&](int e) {
+            if constexpr (kGenSliced) {
+                rope_sincos_b(gk, gr2, gsr, gsv[e], gcv[e]);
+                if constexpr (ROT == kRotHalfGen) {
+                    if (e & 1) {
+                        kc[0][e >> 1] = Elem<T>::pack(gcv[e - 1], gcv[e]);
+                        ks[0][e >> 1] = Elem<T>::pack(gsv[e - 1], gsv[e]);
+                        asm volatile("" ::"v"(kc[0][e >> 1]), "v"(ks[0][e >> 1]));
+                    } else {
+                        asm volatile("" ::"v"(gcv[e]), "v"(gsv[e]));
+                    }
+                } else {
+                    u32x4& tc = e < 4 ? kc[0] : kc2[0];
+                    u32x4& ts = e < 4 ? ks[0] : ks2[0];
+                    tc[e & 3] = Elem<T>::pack(gcv[e], gcv[e]);
+                    ts[e & 3] = Elem<T>::pack(gsv[e], gsv[e]);
+                    asm volatile("" ::"v"(tc[e & 3]), "v"(ts[e & 3]));
+                }
+            }
+        };
+        auto gen_slice = [&](int j) {
+            if constexpr (kGenSliced) {
+                // (the empty asm statements keep each piece here: the values are used only
+                // under a later branch, into which the compiler would otherwise move them)
+                if (j == 0) {
+                    gq = __fdiv_rn((float)kpos[0], a.pos_scale);
+                    asm volatile("" ::"v"(gq));
+                } else if (j & 1) {
+                    const int e = (j - 1) >> 1;
+                    const float th = __fmul_rn(gq, kf[0][e]);  // the angle table_angle forms
+                    gfar |= __builtin_fabsf(th) > kFastPathMax;
+                    rope_sincos_a(th, gk, gr2, gsr);
+                    asm volatile("" ::"v"(gk), "v"(gr2), "v"(gsr));
+                } else {
+                    gen_finish((j - 2) >> 1);
+                }
+            }
+        };
         if (active) {
             // ---- S^T - m = K' Q'^T - m : lane (r, h) gets keys k0 + 32*blk + 16h + i of query qi
             f32x16 sacc[2];
@@ -451,8 +498,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 for (int j = 0; j < NS; ++j) {
                     if (j + SPD < NS) kb[(j + SPD) % (SPD + 1)] = rd_k(j + SPD);
                     sacc[j & 1] = Mfma<T>::run(kb[j % (SPD + 1)], qreg[j >> 1], j < 2 ? minit : sacc[j & 1]);
+                    gen_slice(j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                gen_finish(7);
             }
             // ---- masks: causal (key > query) and the ragged end of the sequence: key
             // k0 + 32*blk + 16h + i is dropped iff it exceeds this lane's last key kmax
@@ -516,7 +565,20 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             l_run += lt;
         }
 
-        constexpr bool kSliced = (ROT == kRotHalfTable || ROT == kRotInterTable) && NKI == 1 && KITEMS == NT && D == 128;
+        if constexpr (kGenSliced) {
+            // waves that skipped the scores, or with an angle beyond the fast path, form the
+            // staged tile's table values here in one piece (rounded to T as rope_tables_ex
+            // stores them, like the pieces above)
+            if (!active || __builtin_amdgcn_ballot_w64(gfar) != 0) {
+                if constexpr (ROT == kRotHalfGen) {
+                    gen_table_chunk<T>(kpos[0], a.pos_scale, kf[0], kc[0], ks[0]);
+                } else {
+                    gen_table_chunk_inter<T>(kpos[0], a.pos_scale, &kf[0][0], kc[0], ks[0]);
+                    gen_table_chunk_inter<T>(kpos[0], a.pos_scale, &kf[0][4], kc2[0], ks2[0]);
+                }
+            }
+        }
+        constexpr bool kSliced = ROT != kRotNone && NKI == 1 && KITEMS == NT && D == 128;
         if constexpr (kSliced) {
             // ---- O^T += V^T P^T, each MFMA followed by a slice of the next tile's K rotation
             // (vector work the matrix core does not wait for); the P.V of inactive waves
@@ -537,7 +599,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             float rx0 = 0.f, rx1 = 0.f, ry0 = 0.f, ry1 = 0.f, rc0 = 0.f, rc1 = 0.f, rs0 = 0.f, rs1 = 0.f;
             u32x4 kxo, kyo;
             auto rot_slice = [&](int sl) {
-                if constexpr (ROT == kRotInterTable) {
+                if constexpr (rot_inter(ROT)) {
                     // word w of the x half (w < 4) or of the y half: unpack, then rotate and pack
                     const int w = sl >> 1;
                     const u32x4& src = w < 4 ? kx[0] : ky[0];
