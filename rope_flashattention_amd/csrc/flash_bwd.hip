@@ -63,13 +63,25 @@ struct BwdArgs {
 };
 
 // Workgroups go to the 8 XCDs round robin by linear id.  The workgroups of one group
-// (those reading the same rows: one (sequence, kv head)) are kept on one XCD and
-// dispatched back to back, so they share that XCD's L2; item = rank within the group.
+// (those reading the same rows: one (sequence, kv head)) are kept on one XCD and start
+// together, so they share that XCD's L2; item = rank within the group, longest first.
+// An XCD's groups are taken K at a time with their items interleaved (item t of each of the
+// K groups, then item t + 1): a group dispatched last would otherwise start its longest
+// items when the XCD is nearly done and leave the other CUs idle at the end.
+template <int K>
 __device__ __forceinline__ void xcd_grouped(int id, int per_group, int ngroups, int& grp, int& item) {
     if ((ngroups & 7) == 0) {
-        const int slot = id >> 3;
-        grp = (id & 7) + 8 * (slot / per_group);
-        item = slot % per_group;
+        const int slot = id >> 3;       // position in this XCD's dispatch order
+        const int G = ngroups >> 3;     // groups per XCD
+        const int span = K * per_group;
+        int chunk = slot / span, kc = K;
+        if (chunk >= G / K) {           // the last, partial chunk of G % K groups
+            chunk = G / K;
+            kc = G - chunk * K;
+        }
+        const int rem = slot - chunk * span;
+        item = rem / kc;
+        grp = (id & 7) + 8 * (chunk * K + rem % kc);
     } else {
         grp = id / per_group;
         item = id - grp * per_group;
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
     int grp, tile;
-    xcd_grouped(blockIdx.x, a.kv_tiles, a.hkv * a.batch, grp, tile);
+    xcd_grouped<2>(blockIdx.x, a.kv_tiles, a.hkv * a.batch, grp, tile);
     const int kvh = grp % a.hkv;
     const int b = grp / a.hkv;
     const BwdSeq sq = bwd_seq(a, b);
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     // group = (sequence, kv head); within it: query tiles longest first, the q heads of the
     // kv head next to each other (they read the same K/V tiles in the same order)
     int grp, item;
-    xcd_grouped(blockIdx.x, a.q_tiles * a.group, a.hkv * a.batch, grp, item);
+    xcd_grouped<4>(blockIdx.x, a.q_tiles * a.group, a.hkv * a.batch, grp, item);
     const int kvh = grp % a.hkv;
     const int b = grp / a.hkv;
     const int qt = a.q_tiles - 1 - item / a.group;
