@@ -30,8 +30,7 @@
 // sets used in turn (a block's loads then have a whole block's compute to arrive), LDS is
 // double-buffered with one barrier per block, and the A operands of the row reads are
 // fetched two products ahead; the workgroups that read the same rows run on one XCD in
-// step.  The epilogues apply M^T
-// (the transposed Rope op) to dq' and dk' before the stores.
+// step.  The epilogues apply M^T (the transposed Rope op) to dq' and dk' before the stores.
 #include <type_traits>
 
 #include "common.h"

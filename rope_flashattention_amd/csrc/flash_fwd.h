@@ -14,9 +14,9 @@
 // Per key tile of 64 keys (LDS double-buffered, one barrier per tile):
 //   * S^T = K' Q'^T with 32x32x16 MFMA: A = K' rows from LDS (read four products ahead),
 //     B = Q' held in registers since the start (rotated and multiplied by
-//     softmax_scale*log2(e) once).  A lane
-//     therefore holds 16 scores of one query row and the row statistics need a single
-//     exchange between the two halves of the wave (v_permlane32_swap).
+//     softmax_scale*log2(e) once).  A lane therefore holds 16 scores of one query row and
+//     the row statistics need a single exchange between the two halves of the wave
+//     (v_permlane32_swap).
 //   * Online softmax in the log2 domain with a lazily updated reference m: the MFMA
 //     accumulator starts at -m (kept in registers), so S - m comes out of the matrix core
 //     and P = exp2(S - m) needs no subtraction and no row max.  The reference (and the O, l
@@ -667,8 +667,8 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             constexpr int NMB = D / 32, NJ = 4 * NMB, PD = 3;
             const T* vp0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
             auto rd_v = [&](int j) {
-                const int ks = j / NMB;
-                const T* vp = vp0 + ((ks >> 1) * 32 + 8 * (ks & 1)) * VP + (j % NMB) * 32;
+                const int kstep = j / NMB;
+                const T* vp = vp0 + ((kstep >> 1) * 32 + 8 * (kstep & 1)) * VP + (j % NMB) * 32;
                 const i16x4 lo = lds_read_tr16(vp);
                 const i16x4 hi = lds_read_tr16(vp + 4 * VP);
                 return __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -680,8 +680,8 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 if (j + PD < NJ) vb[(j + PD) % (PD + 1)] = rd_v(j + PD);
-                const int ks = j / NMB;
-                oacc[j % NMB] = Mfma<T>::run(vb[j % (PD + 1)], pk[ks >> 1][ks & 1], oacc[j % NMB]);
+                const int kstep = j / NMB;
+                oacc[j % NMB] = Mfma<T>::run(vb[j % (PD + 1)], pk[kstep >> 1][kstep & 1], oacc[j % NMB]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
