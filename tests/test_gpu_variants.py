@@ -184,6 +184,36 @@ def test_attention_formed_tables_bit_exact(cfg, pairing):
 
 
 @pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_attention_formed_tables_large_positions(pairing):
+    """Positions near 3e6 (scaled by 1/2: angles up to 1.5e6 rad, past the 2^20 limit of the
+    sine/cosine fast path): the kernel forming its tables takes its fallback for those
+    angles and still equals the call given the tables rope_tables_ex writes for the same
+    positions; both within the attention bar of the oracle."""
+    inp = wl.generate(wl.SMALL[5])                      # GQA 16/2, D 128, bf16, S 520, s = 2
+    w = inp.workload
+    dev = device()
+    D, S = w.head_dim, w.seqlen
+    q, k, v = to_dev(inp)
+    pos_np = (inp.pos[:S].astype(np.int64) + 3_000_000).astype(np.int32)
+    pos = torch.from_numpy(pos_np).to(dev)
+    f = torch.from_numpy(rfa.inv_freq(w.base, D, [S], w.trained_len)).to(dev)
+    s, c = rfa.rope_tables(pos, f, [S], D, w.pos_scale, w.torch_dtype, pairing=pairing)
+    kw = dict(causal=True, softmax_scale=w.softmax_scale, return_lse=True, pairing=pairing)
+    to, tl = rfa.rope_flash_attn_fwd(q, k, v, c, s, **kw)
+    go, gl = rfa.rope_flash_attn_fwd(q, k, v, None, None, pos=pos, inv_freq=f, pos_scale=w.pos_scale, **kw)
+    torch.cuda.synchronize()
+    same = torch.equal(to, go) and torch.equal(tl, gl)
+    fo = orc.inv_freq_per_sequence(w.base, inp.seq_lens, D, w.trained_len)
+    rs, rc = orc.rope_tables(pos_np, fo, inp.seq_lens, w.pos_scale, "fp32", pairing)
+    rs, rc = orc.round_rne(rs, w.dtype), orc.round_rne(rc, w.dtype)
+    qn, kn, vn = inp.packed()
+    ro, rl = orc.rope_attention(qn, kn, vn, rc, rs, inp.seq_lens, w.softmax_scale, True, pairing)
+    err = np.abs(packed_out(inp, go, "BNSD") - ro).max()
+    say(f"attention formed tables, positions ~3e6, {pairing}: equal={same} max-abs {err:.3e}")
+    assert same and err <= ATTN_TOL[w.dtype]
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
 def test_attention_formed_tables_full_size(pairing):
     """The benchmarked workload (qwen7b-like, S 2048) with tables formed in the kernel."""
     inp = wl.generate(wl.CONFIGS[2])
