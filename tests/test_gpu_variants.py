@@ -183,6 +183,30 @@ def test_attention_formed_tables_bit_exact(cfg, pairing):
     assert same
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_attention_head_dim_64_variants(dtype, pairing):
+    """head_dim 64 (the unsliced kernel path) with either pairing, GQA 16/2 (8 q heads per
+    workgroup) and a ragged length: tables read against the oracle, and tables formed in
+    the kernel bit-identical to them."""
+    w = wl.Workload(f"D64 GQA {dtype}", dtype, 2, 16, 2, 64, seqlen=301, base=1e4, seed=5300)
+    inp = wl.generate(w)
+    q, k, v = to_dev(inp)
+    s, c, pos, f, tsr = gpu_tables_for(inp, pairing)
+    kw = dict(causal=True, softmax_scale=w.softmax_scale, table_seq_rows=tsr, return_lse=True, pairing=pairing)
+    to, tl = rfa.rope_flash_attn_fwd(q, k, v, c, s, **kw)
+    go, gl = rfa.rope_flash_attn_fwd(q, k, v, None, None, pos=pos, inv_freq=f, pos_scale=w.pos_scale, **kw)
+    torch.cuda.synchronize()
+    same = torch.equal(to, go) and torch.equal(tl, gl)
+    qn, kn, vn = inp.packed()
+    rs, rc = oracle_tables_for(inp, pairing, w.dtype)
+    ro, rl = orc.rope_attention(qn, kn, vn, rc, rs, inp.seq_lens, w.softmax_scale, True, pairing)
+    err = np.abs(packed_out(inp, to, "BNSD") - ro).max()
+    lerr = np.abs(tl.cpu().numpy().astype(np.float64) - rl).max()
+    say(f"attention D64 {dtype} {pairing}: formed equal={same} max-abs {err:.3e} lse {lerr:.3e}")
+    assert same and err <= ATTN_TOL[w.dtype] and lerr <= ATTN_TOL[w.dtype]
+
+
 @pytest.mark.parametrize("pairing", ["half", "interleaved"])
 def test_attention_formed_tables_large_positions(pairing):
     """Positions near 3e6 (scaled by 1/2: angles up to 1.5e6 rad, past the 2^20 limit of the
