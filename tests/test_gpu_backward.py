@@ -103,6 +103,16 @@ def test_backward_bsnd_layout():
     run_bwd(wl.generate(dataclasses.replace(wl.SMALL[2], seed=5300)), layout="BSND")
 
 
+@pytest.mark.parametrize("batch,hq,hkv", [(3, 8, 8), (5, 16, 8), (3, 16, 4)])
+def test_backward_xcd_group_counts(batch, hq, hkv):
+    """(sequence, kv head) group counts of 24, 40 and 12: three and five groups per XCD (the
+    dK/dV grid takes them two at a time and the dQ grid four at a time, so each has a
+    partial last chunk) and a count that is not a multiple of 8 (plain order)."""
+    w = wl.Workload(f"groups B{batch} H{hq}/{hkv}", "bf16", batch, hq, hkv, 128, seqlen=200, base=1e4,
+                    seed=5600 + batch * hq)
+    run_bwd(wl.generate(w))
+
+
 @pytest.mark.parametrize("S", [1, 31, 32, 33, 127, 128, 129, 257])
 def test_backward_edge_lengths(S):
     w = dataclasses.replace(wl.SMALL[3], seqlen=S, seed=5400 + S)
