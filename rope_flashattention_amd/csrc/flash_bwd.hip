@@ -12,14 +12,15 @@
 //   * bwd_prep_kernel: per (query row, q head) delta and the rotated row q' = M q, per
 //     (key row, kv head) k' = M k, into the workspace (so the two main kernels stage plain
 //     copies; only their epilogues use the tables).
-//   * bwd_dkv_kernel: a workgroup of 4 waves owns 128 keys of one (sequence, kv head); each
-//     wave keeps its 32 keys' rotated K' and V as MFMA B operands in registers and
-//     accumulates dV^T and dK'^T over every q head of the group and every query block of
-//     32 rows that can see its keys.  Per block: S and dP with the 32x32x16 MFMA (A = the
-//     block's Q' and dO rows read from LDS in the permuted row order pi, which leaves each
-//     lane half with 16 consecutive queries of one key), then dV^T += dO^T P and
-//     dK'^T += Q'^T dS with the transposing LDS read (ds_read_b64_tr_b16) supplying
-//     dO^T and Q'^T.
+//   * bwd_dkv_kernel: a workgroup of 8 waves (two per SIMD) owns 128 keys of one (sequence,
+//     kv head) and accumulates dV^T and dK'^T over every q head of the group and every
+//     query block of 32 rows that can see its keys.  Main waves 0-3 keep their 32 keys'
+//     rotated K' and V as MFMA B operands in registers; per block they form S and dP with
+//     the 32x32x16 MFMA (A = the block's Q' and dO rows read from LDS in the permuted row
+//     order pi, which leaves each lane half with 16 consecutive queries of one key), then
+//     P and dS, accumulate dV^T += dO^T P and leave dS in LDS.  Helper waves 4-7 stage the
+//     blocks and, one block later, accumulate dK'^T += Q'^T dS for the keys of main wave
+//     w - 4.  The transposing LDS read (ds_read_b64_tr_b16) supplies dO^T and Q'^T.
 //   * bwd_dq_kernel: a workgroup of 8 waves owns 256 query rows of one (sequence, q head);
 //     each wave keeps its 32 rows' Q' and dO as B operands and, per 64-key tile staged in
 //     LDS (K', V), forms S^T, dP^T and dS^T and accumulates
@@ -28,9 +29,10 @@
 // in natural order for the transposing reads, each at a padded pitch (bank-conflict free
 // reads, constant read offsets).  Each kernel loads its blocks two ahead into two register
 // sets used in turn (a block's loads then have a whole block's compute to arrive), LDS is
-// double-buffered with one barrier per block, and the A operands of the row reads are
-// fetched two products ahead; the workgroups that read the same rows run on one XCD in
-// step.  The epilogues apply M^T (the transposed Rope op) to dq' and dk' before the stores.
+// double-buffered (triple for a copy read one block later) with one barrier per block, and
+// the A operands of the row reads are fetched two products ahead; the workgroups that read
+// the same rows run on one XCD in step.  The epilogues apply M^T (the transposed Rope op)
+// to dq' and dk' before the stores.
 #include <type_traits>
 
 #include "common.h"
@@ -345,24 +347,35 @@ __device__ __forceinline__ void store_trcopy(T* tt, int r, int c, const u32x4& x
 }
 
 // ============================================================================ dk, dv
+// Eight waves, two per SIMD.  Waves 0-3 (main) own 32 keys each: per block they form S and
+// dP, P and dS = P * (dP - delta), accumulate dV^T += dO^T P and leave dS in LDS as the B
+// operands of the dK product.  Waves 4-7 (helpers) stage every block into LDS and, one block
+// later, accumulate dK'^T += Q'^T dS for the keys of main wave w - 4.  A SIMD then holds one
+// wave whose MFMAs can run under the other's vector work; each wave stays within half the
+// SIMD's registers.
 template <typename T, int D, int PAIR>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int NS = D / 16;
     constexpr int HALF = D / 2;
     constexpr int CPR = D / 16;        // chunk pairs per row
     constexpr int QITEMS = 32 * CPR;   // staging items of a 32-row block (<= 256)
+    static_assert(QITEMS <= 256, "one staging item per helper thread");
     constexpr float kLog2e = 1.4426950408889634f;
-    // double-buffered: block i is written to buffer i & 1 while block i - 1 is read
     constexpr int PA = BwdLds<D>::PA, PT = BwdLds<D>::PT;
+    // row copies and the dO^T copy double-buffered (read in the block's own iteration), the
+    // Q'^T copy triple-buffered (read by the helpers one iteration later)
     __shared__ __attribute__((aligned(16))) T sQa[2][32 * PA];
-    __shared__ __attribute__((aligned(16))) T sQt[2][32 * PT];
     __shared__ __attribute__((aligned(16))) T sDa[2][32 * PA];
     __shared__ __attribute__((aligned(16))) T sDt[2][32 * PT];
+    __shared__ __attribute__((aligned(16))) T sQt[3][32 * PT];
+    __shared__ __attribute__((aligned(16))) u32x4 sDS[2][4][2][64];  // dS B operands per key slice and lane
     __shared__ __attribute__((aligned(16))) float sL[2][32];
     __shared__ __attribute__((aligned(16))) float sDel[2][32];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
+    const int l = tid & 63, n = l & 31, hh = l >> 5;
+    const int wk = w & 3;  // key slice
     int grp, tile;
     xcd_grouped<2>(blockIdx.x, a.kv_tiles, a.hkv * a.batch, grp, tile);
     const int kvh = grp % a.hkv;
@@ -371,202 +384,222 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int L = sq.L;
     const int k0 = tile * 128;
     if (k0 >= L) return;  // whole workgroup
-    const int kw0 = k0 + 32 * w;
+    const int kw0 = k0 + 32 * wk;
     const bool active = kw0 < L;
     const int key = min(kw0 + n, L - 1);
 
-    const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
-    const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
-    const T* Qr = reinterpret_cast<const T*>(a.qrot) + sq.tok * D;  // q' rows of this sequence
-    const T* Db = reinterpret_cast<const T*>(a.dout) + sq.bdo;
-
-    // ---- staging role: item (row sr, chunk pair sc) of each 32-row block; rows past the
-    // end re-read the last row (finite values; their P is exactly 0 through lse = +inf)
-    const bool stager = QITEMS >= 256 || tid < QITEMS;
-    const int sr = (tid % QITEMS) / CPR, sc = (tid % CPR) * 8;
-    // Every thread issues its loads unconditionally (no branch around a load, so no wait
-    // is forced at a join); the loaded values are only used at the next block's store.
-    StageItem pre[2];
-    float pre_l[2], pre_d[2];  // raw lse and delta of row (tid & 31) of the block
-    auto load_block = [&](auto slot, int hi, int q0) {
-        constexpr int S = decltype(slot)::value;
-        const int h = kvh * a.group + hi;
-        const int qi = min(q0 + sr, L - 1);
-        stage_load<T>(pre[S], Qr + ((int64_t)h * a.rows + qi) * D, Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], sc,
-                      HALF);
-        const int64_t idx = (int64_t)h * a.lse_stride + sq.tok + min(q0 + (tid & 31), L - 1);
-        pre_l[S] = a.lse[idx];
-        pre_d[S] = a.delta[idx];
-    };
-    auto store_block = [&](auto slot, int buf, int q0) {
-        constexpr int S = decltype(slot)::value;
-        if (stager) {
-            store_rowcopy<T, D>(sQa[buf], sr, sc, pre[S].a0, pre[S].a1);
-            store_trcopy<T, D>(sQt[buf], sr, sc, pre[S].a0, pre[S].a1);
-            store_rowcopy<T, D>(sDa[buf], sr, sc, pre[S].b0, pre[S].b1);
-            store_trcopy<T, D>(sDt[buf], sr, sc, pre[S].b0, pre[S].b1);
-        }
-        if (tid < 32) {
-            // rows past the end get lse = +inf: their P is exactly 0
-            const bool ok = q0 + tid < L;
-            sL[buf][tid] = ok ? pre_l[S] * kLog2e : __builtin_inff();
-            sDel[buf][tid] = ok ? pre_d[S] : 0.0f;
-        }
-    };
-
-    // ---- this lane's key: rotated K' and V as B operands (column n = key, k = d)
-    u32x4 kb[NS], vb[NS];
-    {
-        const T* kp = reinterpret_cast<const T*>(a.krot) + ((int64_t)kvh * a.rows + sq.tok + key) * D;
-        const T* vp = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)key * a.vs[1] + (int64_t)kvh * a.vs[2];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) kb[s] = load_chunk<T>(kp + 16 * s + 8 * hh).w;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
-        // complete these loads here: otherwise the loop's first use would wait for every
-        // load issued after them, the prefetch included
-#pragma unroll
-        for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(vb[s]));
-    }
-
-    f32x16 dvacc[D / 32], dkacc[D / 32];
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dvacc[mb][i] = dkacc[mb][i] = 0.0f;
     const int tr_row = (l & 15) >> 2;
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
     const int mykey = kw0 + n;
     // P of (query qi, this key) is kept iff qi >= qmin
     const int qmin = mykey >= L ? (1 << 30) : (a.causal ? mykey : -(1 << 30));
     const int q_begin = a.causal ? k0 : 0;
-
     // blocks in order: 32-row query blocks from the last one down, and the group's q heads
     // within each; the workgroups of all key tiles of this (sequence, kv head) start
     // together at the last block and stay in step, reading the same rows at the same time
     const int q_last = q_begin + ((L - 1 - q_begin) >> 5) * 32;
-    // Block loads run two blocks ahead, into two register sets used in turn: block j is
-    // stored from its set at iteration j, which then receives block j + 2.
-    int ld_hi = 0, ld_q0 = q_last;  // next block to load
-    auto advance = [&]() {
-        if (++ld_hi == a.group) {
-            ld_hi = 0;
-            ld_q0 -= 32;
+    // the block computes for this slice's keys (wave-uniform)
+    auto runs = [&](int q0) { return active && !(a.causal && q0 + 31 < kw0); };
+    const T* kp = reinterpret_cast<const T*>(a.krot) + ((int64_t)kvh * a.rows + sq.tok + key) * D;
+
+    // G^T += X^T B over one block: X^T by the transposing read of tile xt, B = bk[s]
+    auto accum_t = [&](const T* xt, const u32x4 (&bk)[2], f32x16 (&acc)[D / 32]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb) {
+                const int r = 16 * hh + 8 * s + tr_row;
+                const int e = mb * 32 + tr_col;
+                const i16x4 lo = bwd_tr16(&xt[r * PT + e]);
+                const i16x4 hi = bwd_tr16(&xt[(r + 4) * PT + e]);
+                acc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                                       bk[s], acc[mb]);
+            }
+    };
+
+    if (w < 4) {
+        // ================================================================ main waves
+        u32x4 kb[NS], vb[NS];
+        {
+            const T* vp = reinterpret_cast<const T*>(a.v) + sq.bv + (int64_t)key * a.vs[1] + (int64_t)kvh * a.vs[2];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) kb[s] = load_chunk<T>(kp + 16 * s + 8 * hh).w;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) vb[s] = load_chunk<T>(vp + 16 * s + 8 * hh).w;
+            // complete these loads here: otherwise the loop's first use would wait for
+            // every load issued after them
+#pragma unroll
+            for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(vb[s]));
         }
-    };
-    auto load_next = [&](auto slot) {
-        const bool ok = ld_q0 >= q_begin;
-        load_block(slot, ok ? ld_hi : 0, ok ? ld_q0 : q_begin);  // past the end: a valid dummy, never stored
-        const int q = ld_q0;
-        advance();
-        return q;
-    };
-    int cq0 = load_next(std::integral_constant<int, 0>{});  // block j
-    int nq0 = load_next(std::integral_constant<int, 1>{});  // block j + 1 (below q_begin: none)
-    int buf = 0;
-    auto iter = [&](auto slot) {
-        const int q0 = cq0;
-        store_block(slot, buf, q0);
-        __syncthreads();  // block visible; every read of this buffer two blocks back is done
-        cq0 = nq0;
-        nq0 = load_next(slot);
-        if (active && !(a.causal && q0 + 31 < kw0)) {  // wave-uniform
-            const T* qa = sQa[buf];
-            const T* qt = sQt[buf];
-            const T* da = sDa[buf];
-            const T* dt = sDt[buf];
-            // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i
-            // A operands read two products ahead (a ring of three), so the products do not
-            // wait on one LDS round trip each
-            constexpr int PD = 2;
-            u32x4 aq[PD + 1], ad[PD + 1];
-            auto rd_a = [&](int s) {
-                const int off = n * PA + 16 * s + 8 * hh;
-                aq[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&qa[off]);
-                ad[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&da[off]);
-            };
+        f32x16 dvacc[D / 32];
 #pragma unroll
-            for (int s = 0; s < PD; ++s) rd_a(s);
-            f32x16 sacc, dpacc;
+        for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 16; ++i) dvacc[mb][i] = 0.0f;
+        int cq0 = q_last, chi = 0;  // the current block
+        int buf = 0;
+        for (;;) {
+            const int q0 = cq0;
+            if (++chi == a.group) {
+                chi = 0;
+                cq0 -= 32;
+            }
+            __syncthreads();  // block staged by the helpers
+            if (runs(q0)) {
+                const T* qa = sQa[buf];
+                const T* da = sDa[buf];
+                // ---- S and dP: lane (n, hh) gets key kw0 + n against queries q0 + 16hh + i;
+                // A operands read two products ahead
+                constexpr int PD = 2;
+                u32x4 aq[PD + 1], ad[PD + 1];
+                auto rd_a = [&](int s) {
+                    const int off = n * PA + 16 * s + 8 * hh;
+                    aq[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&qa[off]);
+                    ad[s % (PD + 1)] = *reinterpret_cast<const u32x4*>(&da[off]);
+                };
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s + PD < NS) rd_a(s + PD);
-                sacc = BMma<T>::run(aq[s % (PD + 1)], kb[s], sacc);
-                dpacc = BMma<T>::run(ad[s % (PD + 1)], vb[s], dpacc);
+                for (int s = 0; s < PD; ++s) rd_a(s);
+                f32x16 sacc, dpacc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[i] = dpacc[i] = 0.0f;
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
-            float lv[16], dl[16];
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 4 * i4]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 4 * i4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lv[4 * i4 + e] = l4[e];
-                    dl[4 * i4 + e] = d4[e];
+                for (int s = 0; s < NS; ++s) {
+                    if (s + PD < NS) rd_a(s + PD);
+                    sacc = BMma<T>::run(aq[s % (PD + 1)], kb[s], sacc);
+                    dpacc = BMma<T>::run(ad[s % (PD + 1)], vb[s], dpacc);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-            u32x4 pk[2], dsk[2];
-            auto probs = [&](auto masked) {
+                // ---- P and dS; the mask matters only for blocks that reach this slice's
+                // keys (causal) or for keys past the end
+                const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
+                const bool msk = kw0 + 31 >= L || (a.causal && q0 < kw0 + 31);
+                u32x4 pk[2], dsk[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
+                    const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s]);
+                    const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s + 4]);
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s]);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s + 4]);
                     float p[8], ds[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int i = 8 * s + j;
-                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv[i]));
-                        if (decltype(masked)::value && i < thr) pv = 0.0f;
+                        const float lv = j < 4 ? l0[j] : l1[j - 4];
+                        const float dl = j < 4 ? d0[j] : d1[j - 4];
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv));
+                        pv = (msk && i < thr) ? 0.0f : pv;
                         p[j] = pv;
-                        ds[j] = pv * (dpacc[i] - dl[i]);
+                        ds[j] = pv * (dpacc[i] - dl);
                     }
                     pk[s] = pack<T>(p).w;
                     dsk[s] = pack<T>(ds).w;
+                    sDS[buf][wk][s][l] = dsk[s];
                 }
-            };
-            // the mask matters only for blocks that reach this wave's keys (causal) or
-            // for keys past the end: a wave-uniform choice
-            if (kw0 + 31 >= L || (a.causal && q0 < kw0 + 31))
-                probs(std::true_type{});
-            else
-                probs(std::false_type{});
-            // ---- dV^T += dO^T P,  dK'^T += Q'^T dS
-#pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int r = 16 * hh + 8 * s + tr_row;
-                    const int e = mb * 32 + tr_col;
-                    const i16x4 dlo = bwd_tr16(&dt[r * PT + e]);
-                    const i16x4 dhi = bwd_tr16(&dt[(r + 4) * PT + e]);
-                    dvacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4,
-                                                                                                5, 6, 7)),
-                                             pk[s], dvacc[mb]);
-                    const i16x4 qlo = bwd_tr16(&qt[r * PT + e]);
-                    const i16x4 qhi = bwd_tr16(&qt[(r + 4) * PT + e]);
-                    dkacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4,
-                                                                                                5, 6, 7)),
-                                             dsk[s], dkacc[mb]);
-                }
+                accum_t(sDt[buf], pk, dvacc);  // dV^T += dO^T P
+            }
+            buf ^= 1;
+            if (cq0 < q_begin) break;
         }
-        buf ^= 1;
-        return cq0 >= q_begin;
-    };
-    for (;;) {
-        if (!iter(std::integral_constant<int, 0>{})) break;
-        if (!iter(std::integral_constant<int, 1>{})) break;
-    }
-
-    // ---- epilogue: dk = M^T (s * dK'), dv as accumulated
-    if (active && kw0 + n < L) {
-        const int kr = kw0 + n;
-        T* dkp = reinterpret_cast<T*>(a.dk) + sq.bdk + (int64_t)kr * a.dks[1] + (int64_t)kvh * a.dks[2];
-        T* dvp = reinterpret_cast<T*>(a.dv) + sq.bdv + (int64_t)kr * a.dvs[1] + (int64_t)kvh * a.dvs[2];
-        store_grad_row<T, D, PAIR>(dkacc, a.scale, hh, Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, dkp);
-        store_grad_row<T, D, 0>(dvacc, 1.0f, hh, nullptr, nullptr, dvp);
+        __syncthreads();  // pairs with the helpers' last barrier
+        if (active && kw0 + n < L) {
+            const int kr = kw0 + n;
+            T* dvp = reinterpret_cast<T*>(a.dv) + sq.bdv + (int64_t)kr * a.dvs[1] + (int64_t)kvh * a.dvs[2];
+            store_grad_row<T, D, 0>(dvacc, 1.0f, hh, nullptr, nullptr, dvp);
+        }
+    } else {
+        // ================================================================ helper waves
+        const T* Cg = reinterpret_cast<const T*>(a.cos) + sq.tab * D;
+        const T* Sg = reinterpret_cast<const T*>(a.sin) + sq.tab * D;
+        const T* Qr = reinterpret_cast<const T*>(a.qrot) + sq.tok * D;  // q' rows of this sequence
+        const T* Db = reinterpret_cast<const T*>(a.dout) + sq.bdo;
+        const int ht = tid - 256;
+        // staging: item (row sr, chunk pair sc) of each 32-row block; rows past the end
+        // re-read the last row (finite values; their P is exactly 0 through lse = +inf)
+        const bool stager = ht < QITEMS;
+        const int sr = (ht % QITEMS) / CPR, sc = (ht % CPR) * 8;
+        // Every thread issues its loads unconditionally (no branch around a load, so no
+        // wait is forced at a join); the loaded values are only used at the block's store.
+        StageItem pre[2];
+        float pre_l[2], pre_d[2];  // raw lse and delta of row (ht & 31) of the block
+        auto load_block = [&](auto slot, int hi, int q0) {
+            constexpr int S = decltype(slot)::value;
+            const int h = kvh * a.group + hi;
+            const int qi = min(q0 + sr, L - 1);
+            stage_load<T>(pre[S], Qr + ((int64_t)h * a.rows + qi) * D,
+                          Db + (int64_t)qi * a.dos[1] + (int64_t)h * a.dos[2], sc, HALF);
+            const int64_t idx = (int64_t)h * a.lse_stride + sq.tok + min(q0 + (ht & 31), L - 1);
+            pre_l[S] = a.lse[idx];
+            pre_d[S] = a.delta[idx];
+        };
+        auto store_block = [&](auto slot, int buf, int tbuf, int q0) {
+            constexpr int S = decltype(slot)::value;
+            if (stager) {
+                store_rowcopy<T, D>(sQa[buf], sr, sc, pre[S].a0, pre[S].a1);
+                store_trcopy<T, D>(sQt[tbuf], sr, sc, pre[S].a0, pre[S].a1);
+                store_rowcopy<T, D>(sDa[buf], sr, sc, pre[S].b0, pre[S].b1);
+                store_trcopy<T, D>(sDt[buf], sr, sc, pre[S].b0, pre[S].b1);
+            }
+            if (ht < 32) {
+                // rows past the end get lse = +inf: their P is exactly 0
+                const bool ok = q0 + ht < L;
+                sL[buf][ht] = ok ? pre_l[S] * kLog2e : __builtin_inff();
+                sDel[buf][ht] = ok ? pre_d[S] : 0.0f;
+            }
+        };
+        f32x16 dkacc[D / 32];
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dkacc[mb][i] = 0.0f;
+        // dK'^T += Q'^T dS of a block computed by the main wave of this slice
+        auto dk_block = [&](int pbuf, int ptbuf) {
+            const u32x4 dsk[2] = {sDS[pbuf][wk][0][l], sDS[pbuf][wk][1][l]};
+            accum_t(sQt[ptbuf], dsk, dkacc);
+        };
+        // Block loads run two blocks ahead, into two register sets used in turn: block j
+        // is stored from its set at iteration j, which then receives block j + 2.
+        int ld_hi = 0, ld_q0 = q_last;  // next block to load
+        auto load_next = [&](auto slot) {
+            const bool ok = ld_q0 >= q_begin;
+            load_block(slot, ok ? ld_hi : 0, ok ? ld_q0 : q_begin);  // past the end: a valid dummy, never stored
+            const int q = ld_q0;
+            if (++ld_hi == a.group) {
+                ld_hi = 0;
+                ld_q0 -= 32;
+            }
+            return q;
+        };
+        int cq0 = load_next(std::integral_constant<int, 0>{});  // block j
+        int nq0 = load_next(std::integral_constant<int, 1>{});  // block j + 1 (below q_begin: none)
+        int buf = 0, tbuf = 0;
+        bool prev = false;  // the previous block ran on this slice: its dK product is due
+        int pbuf = 0, ptbuf = 0;
+        auto iter = [&](auto slot) {
+            const int q0 = cq0;
+            store_block(slot, buf, tbuf, q0);
+            __syncthreads();  // block visible; the previous block's dS is in LDS
+            cq0 = nq0;
+            nq0 = load_next(slot);
+            if (prev) dk_block(pbuf, ptbuf);
+            prev = runs(q0);
+            pbuf = buf;
+            ptbuf = tbuf;
+            buf ^= 1;
+            tbuf = tbuf == 2 ? 0 : tbuf + 1;
+            return cq0 >= q_begin;
+        };
+        for (;;) {
+            if (!iter(std::integral_constant<int, 0>{})) break;
+            if (!iter(std::integral_constant<int, 1>{})) break;
+        }
+        __syncthreads();  // the last block's dS is in LDS
+        if (prev) dk_block(pbuf, ptbuf);
+        if (active && kw0 + n < L) {
+            const int kr = kw0 + n;
+            T* dkp = reinterpret_cast<T*>(a.dk) + sq.bdk + (int64_t)kr * a.dks[1] + (int64_t)kvh * a.dks[2];
+            store_grad_row<T, D, PAIR>(dkacc, a.scale, hh, Cg + (int64_t)kr * D, Sg + (int64_t)kr * D, dkp);
+        }
     }
 }
 
@@ -762,7 +795,7 @@ static void launch_bwd_typed(const BwdArgs& a, int maxlen, hipStream_t stream) {
     BwdArgs g = a;
     g.kv_tiles = (maxlen + 127) / 128;
     g.q_tiles = (maxlen + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3((unsigned)(g.kv_tiles * a.hkv * a.batch)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, PAIR>), dim3((unsigned)(g.kv_tiles * a.hkv * a.batch)), dim3(512), 0,
                        stream, g);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, PAIR, NW, KT>), dim3((unsigned)(g.q_tiles * a.hq * a.batch)), dim3(NW * 64),
                        0, stream, g);
