@@ -471,31 +471,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 // ---- P and dS; the mask matters only for blocks that reach this slice's
-                // keys (causal) or for keys past the end
+                // keys (causal) or for keys past the end: a wave-uniform choice between two
+                // copies of this code
                 const int thr = qmin - (q0 + 16 * hh);  // query q0 + 16hh + i is masked iff i < thr
-                const bool msk = kw0 + 31 >= L || (a.causal && q0 < kw0 + 31);
                 u32x4 pk[2], dsk[2];
+                auto probs = [&](auto masked) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s]);
-                    const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s + 4]);
-                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s]);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s + 4]);
-                    float p[8], ds[8];
+                    for (int s = 0; s < 2; ++s) {
+                        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s]);
+                        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sL[buf][16 * hh + 8 * s + 4]);
+                        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s]);
+                        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sDel[buf][16 * hh + 8 * s + 4]);
+                        float p[8], ds[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int i = 8 * s + j;
-                        const float lv = j < 4 ? l0[j] : l1[j - 4];
-                        const float dl = j < 4 ? d0[j] : d1[j - 4];
-                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv));
-                        pv = (msk && i < thr) ? 0.0f : pv;
-                        p[j] = pv;
-                        ds[j] = pv * (dpacc[i] - dl);
+                        for (int j = 0; j < 8; ++j) {
+                            const int i = 8 * s + j;
+                            const float lv = j < 4 ? l0[j] : l1[j - 4];
+                            const float dl = j < 4 ? d0[j] : d1[j - 4];
+                            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.scale_log2, -lv));
+                            if (decltype(masked)::value && i < thr) pv = 0.0f;
+                            p[j] = pv;
+                            ds[j] = pv * (dpacc[i] - dl);
+                        }
+                        pk[s] = pack<T>(p).w;
+                        dsk[s] = pack<T>(ds).w;
+                        sDS[buf][wk][s][l] = dsk[s];
                     }
-                    pk[s] = pack<T>(p).w;
-                    dsk[s] = pack<T>(ds).w;
-                    sDS[buf][wk][s][l] = dsk[s];
-                }
+                };
+                if (kw0 + 31 >= L || (a.causal && q0 < kw0 + 31))
+                    probs(std::true_type{});
+                else
+                    probs(std::false_type{});
                 accum_t(sDt[buf], pk, dvacc);  // dV^T += dO^T P
             }
             buf ^= 1;
