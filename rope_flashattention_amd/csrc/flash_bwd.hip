@@ -627,7 +627,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) T sVa[2][KT * PA];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, n = l & 31, hh = l >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
+    const int l = tid & 63, n = l & 31, hh = l >> 5;
     // group = (sequence, kv head); within it: query tiles longest first, the q heads of the
     // kv head next to each other (they read the same K/V tiles in the same order)
     int grp, item;
