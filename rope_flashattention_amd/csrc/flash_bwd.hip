@@ -402,21 +402,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     auto runs = [&](int q0) { return active && !(a.causal && q0 + 31 < kw0); };
     const T* kp = reinterpret_cast<const T*>(a.krot) + ((int64_t)kvh * a.rows + sq.tok + key) * D;
 
-    // G^T += X^T B over one block: X^T by the transposing read of tile xt, B = bk[s]
-    auto accum_t = [&](const T* xt, const u32x4 (&bk)[2], f32x16 (&acc)[D / 32]) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int mb = 0; mb < D / 32; ++mb) {
-                const int r = 16 * hh + 8 * s + tr_row;
-                const int e = mb * 32 + tr_col;
-                const i16x4 lo = bwd_tr16(&xt[r * PT + e]);
-                const i16x4 hi = bwd_tr16(&xt[(r + 4) * PT + e]);
-                acc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
-                                       bk[s], acc[mb]);
-            }
-    };
-
     if (w < 4) {
         // ================================================================ main waves
         u32x4 kb[NS], vb[NS];
@@ -470,6 +455,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
                     dpacc = BMma<T>::run(ad[s % (PD + 1)], vb[s], dpacc);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                // dO^T operands of the dV products, read now so that they arrive during the
+                // vector work below
+                u32x4 dvop[2][D / 32];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int mb = 0; mb < D / 32; ++mb) {
+                        const T* xt = sDt[buf];
+                        const int r = 16 * hh + 8 * s + tr_row;
+                        const int e = mb * 32 + tr_col;
+                        const i16x4 lo = bwd_tr16(&xt[r * PT + e]);
+                        const i16x4 hi = bwd_tr16(&xt[(r + 4) * PT + e]);
+                        dvop[s][mb] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                __builtin_amdgcn_sched_barrier(0);
                 // ---- P and dS; the mask matters only for blocks that reach this slice's
                 // keys (causal) or for keys past the end: a wave-uniform choice between two
                 // copies of this code
@@ -502,7 +502,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
                     probs(std::true_type{});
                 else
                     probs(std::false_type{});
-                accum_t(sDt[buf], pk, dvacc);  // dV^T += dO^T P
+                // dV^T += dO^T P
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int mb = 0; mb < D / 32; ++mb) dvacc[mb] = BMma<T>::run(dvop[s][mb], pk[s], dvacc[mb]);
             }
             buf ^= 1;
             if (cq0 < q_begin) break;
@@ -561,7 +565,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         // dK'^T += Q'^T dS of a block computed by the main wave of this slice
         auto dk_block = [&](int pbuf, int ptbuf) {
             const u32x4 dsk[2] = {sDS[pbuf][wk][0][l], sDS[pbuf][wk][1][l]};
-            accum_t(sQt[ptbuf], dsk, dkacc);
+            // every Q'^T operand first, then the products back to back
+            u32x4 qop[2][D / 32];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int mb = 0; mb < D / 32; ++mb) {
+                    const T* xt = sQt[ptbuf];
+                    const int r = 16 * hh + 8 * s + tr_row;
+                    const int e = mb * 32 + tr_col;
+                    const i16x4 lo = bwd_tr16(&xt[r * PT + e]);
+                    const i16x4 hi = bwd_tr16(&xt[(r + 4) * PT + e]);
+                    qop[s][mb] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int mb = 0; mb < D / 32; ++mb) dkacc[mb] = BMma<T>::run(qop[s][mb], dsk[s], dkacc[mb]);
         };
         // Block loads run two blocks ahead, into two register sets used in turn: block j
         // is stored from its set at iteration j, which then receives block j + 2.
