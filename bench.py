@@ -2,8 +2,10 @@
 """Benchmark of the fused RoPE + FlashAttention forward on one MI355X.
 
 One step = the whole hot path on one batch of synthetic inputs already resident in HBM:
-rope_tables (cos/sin for positions 0..S-1) followed by rope_flash_attn_fwd (rotation of
-Q/K in registers, causal attention).  The host inverse frequencies are computed once at
+rope_tables (cos/sin for positions 0..S-1) followed by the fused forward
+(rope_flash_attn_fwd_ws: Q rotated in registers; K rotated in the kernel's staging or, where
+that repeats the rotation of a key many times, once per key by a pre-pass into the
+workspace; causal attention).  The host inverse frequencies are computed once at
 set-up (a model-load-time quantity).  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
@@ -11,10 +13,11 @@ set-up (a model-load-time quantity).  Prints one JSON line.
 The default workload is the largest single-GPU one: B1, 64 q heads over 8 kv heads,
 head_dim 128, S 16384, bf16, linear position scaling 2.  The value is TFLOP/s of causal
 attention (4*B*Hq*S^2*D/2 per step) over the timed steps.  The roofline object reports
-the attention kernel's own time, measured with HIP events on the stream it runs on,
-against the dense bf16 MFMA peak.  Extra measurements (after the timed region): the
-fusion ablation (fused kernel against rope_qk + attention without rotation, timed in
-alternating rounds after the same warm-up) on every 16-bit workload, rope_tables GB/s at
+the fused call's own time (its k' pre-pass included), measured with HIP events on the
+stream it runs on, against the dense bf16 MFMA peak.  Extra measurements (after the timed
+region): the fusion ablation (the fused call, the fused kernel rotating K in-loop, and
+rope_qk + attention without rotation, timed in alternating rounds after the same warm-up)
+on every 16-bit workload, rope_tables GB/s at
 the op's size limits, rope_qk GB/s, the RoPE variants of the fused kernel, the backward
 pass, the fused RMSNorm + RoPE + KV-cache write GB/s on a paged-cache prefill, and
 decode-step attention GB/s over a paged cache.  The cpu_baseline leg times the fp64 CPU
@@ -36,7 +39,8 @@ METRIC = "fused RoPE+FlashAttn fwd TFLOP/s and % bf16 MFMA peak; rope_tables GB/
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA peaks (f32: matrix fp32)
 PEAK_HBM_GBS = 8000.0
 EXTRAS = ("ablation", "backward", "variants", "tables", "kvcache", "decode")
-KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.h", "rope_flashattention_amd/csrc/common.h"]
+KERNEL_SOURCES = ["rope_flashattention_amd/csrc/flash_fwd.h", "rope_flashattention_amd/csrc/common.h",
+                  "rope_flashattention_amd/csrc/rope_qk.hip"]
 
 
 def source_hash(paths):
@@ -175,34 +179,42 @@ def attention_setup(w, inp, dev, rfa, wl, np, torch):
     sin = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
     cos = torch.empty((T_tab, D), dtype=w.torch_dtype, device=dev)
     out = torch.empty_like(q)
-    return dict(q=q, k=k, v=v, f=f, pos=pos, tab_lens=tab_lens, sin=sin, cos=cos, out=out, akw=akw)
+    # the fused call's workspace (k' rows of the pre-pass), allocated once
+    need = rfa.flash_attn_fwd_workspace_size(q, k, v, cos, sin, causal=w.causal, **akw)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    return dict(q=q, k=k, v=v, f=f, pos=pos, tab_lens=tab_lens, sin=sin, cos=cos, out=out, akw=akw, ws=ws)
 
 
 def fusion_ablation(w, st, rfa, torch, rounds=5, reps=10):
-    """Fused attention against the unfused path (rope_qk, then attention without rotation),
-    timed in alternating rounds of back-to-back launches after the same warm-up, so that
-    both legs see the same clock state.  Returns medians over the rounds (ms)."""
+    """The fused call (k' pre-pass where the library plans one), the fused kernel rotating K
+    in-loop, and the unfused path (rope_qk, then attention without rotation), timed in
+    alternating rounds of back-to-back calls after the same warm-up, so that every leg sees
+    the same clock state.  Returns medians over the rounds (ms)."""
     q, k, v, cos, sin, out, akw = st["q"], st["k"], st["v"], st["cos"], st["sin"], st["out"], st["akw"]
+    ws = st["ws"] if st["ws"] is not None else "auto"
     qkw = {kk: vv for kk, vv in akw.items()}
     oq, ok = torch.empty_like(q), torch.empty_like(k)
-    fused = lambda: rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
-                                            out=out, **akw)
+    kw = dict(causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+    fused = lambda: rfa.rope_flash_attn_fwd(q, k, v, cos, sin, workspace=ws, **kw)
+    inloop = lambda: rfa.rope_flash_attn_fwd(q, k, v, cos, sin, workspace=None, **kw)
     rot = lambda: rfa.rope_qk(q, k, cos, sin, table_seq_rows=0, out_q=oq, out_k=ok, **qkw)
-    plain = lambda: rfa.rope_flash_attn_fwd(oq, ok, v, None, None, causal=w.causal, softmax_scale=w.softmax_scale,
-                                            out=out, **akw)
+    plain = lambda: rfa.rope_flash_attn_fwd(oq, ok, v, None, None, workspace=None, **kw)
     rot()
     for _ in range(reps):
         fused()
+        inloop()
         plain()
-    tf, tr, tp = [], [], []
+    tf, ti, tr, tp = [], [], [], []
     for _ in range(rounds):
         tf.append(time_events(fused, reps, torch))
+        ti.append(time_events(inloop, reps, torch))
         tr.append(time_events(rot, reps, torch))
         tp.append(time_events(plain, reps, torch))
     del oq, ok
-    mf, mr, mp = median(tf), median(tr), median(tp)
-    return {"fused_ms": round(mf, 4), "rope_qk_ms": round(mr, 4), "plain_attention_ms": round(mp, 4),
-            "unfused_ms": round(mr + mp, 4), "fused_over_unfused": round(mf / (mr + mp), 4)}
+    mf, mi, mr, mp = median(tf), median(ti), median(tr), median(tp)
+    return {"fused_ms": round(mf, 4), "k_prepass": st["ws"] is not None, "fused_in_loop_ms": round(mi, 4),
+            "rope_qk_ms": round(mr, 4), "plain_attention_ms": round(mp, 4), "unfused_ms": round(mr + mp, 4),
+            "fused_over_unfused": round(mf / (mr + mp), 4), "in_loop_over_unfused": round(mi / (mr + mp), 4)}
 
 
 def main():
@@ -257,16 +269,19 @@ def main():
     st = attention_setup(w, inp, dev, rfa, wl, np, torch)
     q, k, v, f, pos, tab_lens = st["q"], st["k"], st["v"], st["f"], st["pos"], st["tab_lens"]
     sin, cos, out, akw = st["sin"], st["cos"], st["out"], st["akw"]
+    ws = st["ws"] if st["ws"] is not None else "auto"
 
     def step():
         rfa.rope_tables(pos, f, tab_lens, D, w.pos_scale, w.torch_dtype, sin, cos)
-        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out,
+                                workspace=ws, **akw)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps; attention launches bracketed by events on their stream
+    # ---- timed region: exactly K steps; each fused call (k' pre-pass and attention kernel)
+    # bracketed by events on its stream
     # (two events per step: each recorded event adds a few microseconds of queue work, so
     # the table pass is timed on its own after this region)
     K = args.steps
@@ -276,7 +291,8 @@ def main():
     for i in range(K):
         rfa.rope_tables(pos, f, tab_lens, D, w.pos_scale, w.torch_dtype, sin, cos)
         ev[i][0].record()
-        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out, **akw)
+        rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale, out=out,
+                                workspace=ws, **akw)
         ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -316,7 +332,9 @@ def main():
                    "ntk_trained_len": w.trained_len, "pos_scale": w.pos_scale, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": read_traffic(wkey),
-                     "kernel": "flash_fwd16_kernel", "avg_launch_ms": round(att_ms, 4)},
+                     "kernel": ("rope_qk_kernel (k' pre-pass) + flash_fwd16_kernel, timed together"
+                                if st["ws"] is not None else "flash_fwd16_kernel"),
+                     "avg_launch_ms": round(att_ms, 4)},
         "components": {"rope_tables_ms": round(tab_ms, 5), "attention_ms": round(att_ms, 4),
                        "attention_ms_p10_median_p90": [round(att_all[int(0.1 * (K - 1))], 4),
                                                        round(median(att_all), 4),
@@ -376,7 +394,7 @@ def main():
             # recomputation of S and dP is overhead, not counted)
             if w.dtype != "f32":
                 out_f, lse_f = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, causal=w.causal, softmax_scale=w.softmax_scale,
-                                                       return_lse=True, **akw)
+                                                       return_lse=True, workspace=ws, **akw)
                 bdo = wl.generate_dout(inp, 9001).to(dev)
                 if not w.varlen and akw.get("layout") == "BSND":
                     bdo = bdo.transpose(1, 2).contiguous()

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ROPE_FA_ABI_VERSION 2
+#define ROPE_FA_ABI_VERSION 3
 
 typedef enum rope_status {
     ROPE_OK = 0,
@@ -257,6 +257,34 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream);
  * Errors: NULL, SHAPE, DTYPE, LIMIT, UNSUPPORTED, ABI, HIP.  One kernel launch.
  */
 rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream);
+
+/*
+ * rope_flash_attn_fwd_ws — the same operation and result as rope_flash_attn_fwd (bit for bit),
+ * with a caller-owned workspace that lets the library rotate each key once instead of in
+ * every workgroup that stages it.  The fused kernel of [RoPE-fusion blog], section 三,
+ * rotates a K tile wherever it is staged; a kv head's key is staged by every query tile and
+ * head group that reaches it, so on long sequences the repeated rotation costs more than
+ * one HBM round trip of k' (hkv heads: under GQA a fraction of q's bytes), which this call
+ * accepts while q' still never reaches HBM.  When rope_flash_attn_fwd_workspace_size(p) > 0
+ * the call runs two launches on hip_stream: a pre-pass that writes k' = rope(k) of every
+ * key row and kv head (the rope_qk formula and rounding, reading only table columns
+ * [0, head_dim/2) with ROPE_PAIR_HALF, as the fused kernel does) into the workspace, then
+ * the fused kernel with q rotated in registers as before and the k' tiles staged as they
+ * are; rotated q never leaves the registers.  When the size is 0 (no rotation, F32, short
+ * sequences where in-loop rotation is cheaper, or varlen with tables formed from
+ * per-sequence inverse frequencies) it is rope_flash_attn_fwd and the workspace is unused.
+ * workspace: DEVICE, 256-byte aligned, >= the size, not overlapping any input or output;
+ * after the call it holds k' of dtype as [batch, hkv, seqlen, head_dim] (dense) or
+ * [hkv, ntokens, head_dim] (varlen) and is only used by this call's kernels (reuse it once
+ * the stream has passed them).  Errors: those of rope_flash_attn_fwd, and ROPE_ERR_WORKSPACE when the size
+ * is > 0 and the workspace is NULL, misaligned or smaller.
+ */
+rope_status rope_flash_attn_fwd_ws(const rope_attn_params* p, void* workspace, uint64_t workspace_bytes,
+                                   void* hip_stream);
+
+/* Workspace bytes rope_flash_attn_fwd_ws uses for these parameters (0: none, in-loop
+ * rotation), or 0 when the parameters are invalid.  Host only. */
+uint64_t rope_flash_attn_fwd_workspace_size(const rope_attn_params* p);
 
 /*
  * Parameters of rope_flash_attn_bwd: the forward call's parameters plus the gradients.

@@ -26,6 +26,7 @@ __all__ = [
     "rope_tables",
     "rope_qk",
     "rope_flash_attn_fwd",
+    "flash_attn_fwd_workspace_size",
     "rope_flash_attn_bwd",
     "rope_kv_rms_norm_rope_cache",
     "rope_decode_attn_fwd",
@@ -48,7 +49,7 @@ STATUS = {0: "ROPE_OK", 1: "ROPE_ERR_NULL", 2: "ROPE_ERR_SHAPE", 3: "ROPE_ERR_DT
 DTYPE = {None: 0, torch.float16: 1, torch.bfloat16: 2, torch.float32: 3}
 PAIRING = {"half": 0, "interleaved": 1}
 ANGLE_MODE = {"f32": 0, "exact": 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class RopeError(RuntimeError):
@@ -206,6 +207,10 @@ def lib() -> ctypes.CDLL:
     L.rope_qk.restype = st
     L.rope_flash_attn_fwd.argtypes = [ctypes.POINTER(RopeAttnParams), vp]
     L.rope_flash_attn_fwd.restype = st
+    L.rope_flash_attn_fwd_ws.argtypes = [ctypes.POINTER(RopeAttnParams), vp, ctypes.c_uint64, vp]
+    L.rope_flash_attn_fwd_ws.restype = st
+    L.rope_flash_attn_fwd_workspace_size.argtypes = [ctypes.POINTER(RopeAttnParams)]
+    L.rope_flash_attn_fwd_workspace_size.restype = ctypes.c_uint64
     L.rope_kv_rms_norm_rope_cache.argtypes = [ctypes.POINTER(RopeKvCacheParams), vp]
     L.rope_kv_rms_norm_rope_cache.restype = st
     L.rope_kv_cache_params_size.restype = ctypes.c_uint32
@@ -416,11 +421,15 @@ def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: 
                         cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
                         table_seq_rows: int = 0, return_lse: bool = False, out: Optional[torch.Tensor] = None,
                         pairing: str = "half", pos: Optional[torch.Tensor] = None,
-                        inv_freq: Optional[torch.Tensor] = None, pos_scale: float = 1.0):
+                        inv_freq: Optional[torch.Tensor] = None, pos_scale: float = 1.0,
+                        workspace="auto"):
     """Attention output (and lse [hq, ntokens] float32 if asked).
 
     cos = sin = None: no rotation, unless pos / inv_freq are given, in which case the kernel
-    forms the table values itself.
+    forms the table values itself.  workspace: "auto" calls rope_flash_attn_fwd_ws with a
+    workspace of the size the library asks for (none when it rotates K in-loop), a uint8
+    device tensor calls it with that buffer, None calls rope_flash_attn_fwd (K rotated in
+    every workgroup that stages it).  All three give the same bits.
     """
     _need_cuda(q, k, v, cos, sin, cu_seqlens, out, pos, inv_freq)
     p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
@@ -441,8 +450,40 @@ def rope_flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: 
     if return_lse:
         lse = torch.empty((p.hq, p.ntokens), dtype=torch.float32, device=q.device)
         p.lse = lse.data_ptr()
-    _check("rope_flash_attn_fwd", lib().rope_flash_attn_fwd(ctypes.byref(p), _stream(q)))
+    if workspace is None:
+        _check("rope_flash_attn_fwd", lib().rope_flash_attn_fwd(ctypes.byref(p), _stream(q)))
+        return (out, lse) if return_lse else out
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', a device tensor or None")
+        need = int(lib().rope_flash_attn_fwd_workspace_size(ctypes.byref(p)))
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    elif workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
+    ptr = workspace.data_ptr() if workspace is not None else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rope_flash_attn_fwd_ws", lib().rope_flash_attn_fwd_ws(ctypes.byref(p), ptr, nbytes, _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def flash_attn_fwd_workspace_size(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  cos: Optional[torch.Tensor] = None, sin: Optional[torch.Tensor] = None, *,
+                                  causal: bool = True, layout: str = "BNSD", cu_seqlens: Optional[torch.Tensor] = None,
+                                  max_seqlen: Optional[int] = None, table_seq_rows: int = 0, pairing: str = "half",
+                                  pos: Optional[torch.Tensor] = None, inv_freq: Optional[torch.Tensor] = None,
+                                  pos_scale: float = 1.0) -> int:
+    """Bytes rope_flash_attn_fwd_ws would use for this call (0: K rotated in-loop)."""
+    p = _params(q, k, layout, cos, sin, cu_seqlens, max_seqlen, table_seq_rows)
+    p.pairing = PAIRING[pairing]
+    if cos is None and pos is not None:
+        _gen_tables(p, pos, inv_freq, pos_scale, p.head_dim)
+    p.v = v.data_ptr()
+    p.out = q.data_ptr()  # a stand-in: the size depends on the shapes only
+    p.v_stride[:] = _strides(v, layout)
+    p.o_stride[:] = _strides(q, layout)
+    p.causal = 1 if causal else 0
+    p.softmax_scale = 1.0 / q.shape[-1] ** 0.5
+    return int(lib().rope_flash_attn_fwd_workspace_size(ctypes.byref(p)))
 
 
 # --------------------------------------------------------------------------- rope_flash_attn_bwd

@@ -19,7 +19,9 @@ hipError_t launch_rope_tables(const int32_t* pos, const float* inv_freq, const i
                               int32_t ntokens, int32_t head_size, float pos_scale, rope_dtype out_dtype,
                               int pairing, int angle_mode, void* sin_out, void* cos_out, hipStream_t stream);
 hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream);
-hipError_t launch_flash_fwd(const rope_attn_params* p, hipStream_t stream);
+hipError_t launch_flash_fwd(const rope_attn_params* p, const void* kprime, hipStream_t stream);
+hipError_t launch_rope_k_prepass(const rope_attn_params* p, void* kout, hipStream_t stream);
+uint64_t flash_fwd_workspace_bytes(const rope_attn_params* p);
 hipError_t launch_kv_cache(const rope_kv_cache_params* p, hipStream_t stream);
 hipError_t launch_decode(const rope_decode_params* p, hipStream_t stream);
 hipError_t launch_flash_bwd(const rope_attn_bwd_params* p, hipStream_t stream);
@@ -350,7 +352,29 @@ rope_status rope_qk(const rope_attn_params* p, void* hip_stream) {
 rope_status rope_flash_attn_fwd(const rope_attn_params* p, void* hip_stream) {
     const rope_status st = check_params(p, true);
     if (st != ROPE_OK) return st;
-    const hipError_t e = ropefa::launch_flash_fwd(p, (hipStream_t)hip_stream);
+    const hipError_t e = ropefa::launch_flash_fwd(p, nullptr, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+uint64_t rope_flash_attn_fwd_workspace_size(const rope_attn_params* p) {
+    if (check_params(p, true) != ROPE_OK) return 0;
+    return ropefa::flash_fwd_workspace_bytes(p);
+}
+
+rope_status rope_flash_attn_fwd_ws(const rope_attn_params* p, void* workspace, uint64_t workspace_bytes,
+                                   void* hip_stream) {
+    const rope_status st = check_params(p, true);
+    if (st != ROPE_OK) return st;
+    const uint64_t need = ropefa::flash_fwd_workspace_bytes(p);
+    hipError_t e;
+    if (need == 0) {
+        e = ropefa::launch_flash_fwd(p, nullptr, (hipStream_t)hip_stream);
+    } else {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
+            return ROPE_ERR_WORKSPACE;
+        e = ropefa::launch_rope_k_prepass(p, workspace, (hipStream_t)hip_stream);
+        if (e == hipSuccess) e = ropefa::launch_flash_fwd(p, workspace, (hipStream_t)hip_stream);
+    }
     return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 

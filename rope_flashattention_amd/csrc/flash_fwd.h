@@ -35,6 +35,13 @@
 //     staged tile's columns are likewise computed in pieces between the score MFMAs.  No
 //     v_dot2 anywhere: on gfx950 those run in the matrix-core pipeline and would serialise
 //     with the MFMAs.
+// K rotated once per key instead (modes kRotQ*): every workgroup of a kv head stages each
+// key tile it needs, so in-loop rotation repeats the rotation of a key once per query tile
+// and head group that reaches it (about 256 times on a causal 16384-token GQA sequence
+// with 8 q heads per kv head).  Where that repetition costs more than one pass over K, the
+// host runs a pre-pass that writes k' (the same arithmetic and rounding as the in-loop
+// rotation, so the results are bit-identical) and launches these modes, which rotate only
+// Q in registers and stage k' tiles as they are.
 // Permuted K' rows: MFMA result row m of S^T is key pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3)
 // inside a 32-key block, which makes the 16 scores of lane half h the contiguous keys
 // 16h .. 16h+15; K' for key pi(m) is stored at LDS row m so the MFMA reads consecutive rows.
@@ -76,10 +83,18 @@ enum RotMode : int {
     kRotHalfTable = 1,    // rotate-half pairs, tables read (columns [0, D/2) only)
     kRotInterTable = 2,   // interleaved pairs, tables read (all columns)
     kRotHalfGen = 3,      // rotate-half pairs, table values formed in the kernel
-    kRotInterGen = 4      // interleaved pairs, table values formed in the kernel
+    kRotInterGen = 4,     // interleaved pairs, table values formed in the kernel
+    // Q rotated in the kernel as by mode m - 4; K read already rotated (a pre-pass wrote k'
+    // once per key, instead of every workgroup rotating each tile it stages)
+    kRotQHalfTable = 5,
+    kRotQInterTable = 6,
+    kRotQHalfGen = 7,
+    kRotQInterGen = 8
 };
 constexpr bool rot_inter(int rot) { return rot == kRotInterTable || rot == kRotInterGen; }
 constexpr bool rot_gen(int rot) { return rot == kRotHalfGen || rot == kRotInterGen; }
+constexpr int q_rot(int rot) { return rot >= kRotQHalfTable ? rot - 4 : rot; }  // rotation of Q
+constexpr int k_rot(int rot) { return rot >= kRotQHalfTable ? kRotNone : rot; } // of staged K tiles
 
 // Table values formed in the kernel, rounded to T as a stored table would be:
 // cos/sin of frequencies f[0..7] at position p, packed.
@@ -185,9 +200,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     constexpr int NKI = (KITEMS + NT - 1) / NT;
     constexpr int NVI = (VITEMS + NT - 1) / NT;
     constexpr float kLazySum = 65536.0f;          // tile row sum that forces the reference to move
+    constexpr int QROT = q_rot(ROT), KROT = k_rot(ROT);
     // formed tables at head_dim 128: the staged tile's sin/cos are computed between the score
     // MFMAs and its rotation between the P.V MFMAs
-    constexpr bool kGenSliced = rot_gen(ROT) && NKI == 1 && KITEMS == NT && D == 128;
+    constexpr bool kGenSliced = rot_gen(KROT) && NKI == 1 && KITEMS == NT && D == 128;
     typedef typename Mfma<T>::vec vec;
 
     __shared__ __attribute__((aligned(16))) T sK[2][kBN * KP];
@@ -223,14 +239,14 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     u32x4 kx[NKI], ky[NKI], kc[NKI], ks[NKI], kc2[NKI], ks2[NKI], vr[NVI];
     int32_t kpos[NKI];
     float kf[NKI][8];  // formed tables: this thread's frequencies (fixed per item slot)
-    if constexpr (rot_gen(ROT)) {
+    if constexpr (rot_gen(KROT)) {
 #pragma unroll
         for (int j = 0; j < NKI; ++j) {
             const int it = tid + j * NT;
             const int c = (it % KCH) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                kf[j][e] = ROT == kRotHalfGen ? Fg[c + e] : Fg[(e < 4 ? c : c + HALF) / 2 + (e & 3)];
+                kf[j][e] = KROT == kRotHalfGen ? Fg[c + e] : Fg[(e < 4 ? c : c + HALF) / 2 + (e & 3)];
         }
     }
     // Byte offsets of this thread's staged chunks within a full tile (32-bit, non-negative),
@@ -266,15 +282,15 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 const uint32_t to = full ? tob[j] : (uint32_t)(kap * D + c) * (uint32_t)sizeof(T);
                 kx[j] = *reinterpret_cast<const u32x4*>(kg + ko);
                 ky[j] = *reinterpret_cast<const u32x4*>(kg + ko + HALF * sizeof(T));
-                if constexpr (ROT == kRotHalfTable || ROT == kRotInterTable) {
+                if constexpr (KROT == kRotHalfTable || KROT == kRotInterTable) {
                     kc[j] = *reinterpret_cast<const u32x4*>(cg + to);
                     ks[j] = *reinterpret_cast<const u32x4*>(sg + to);
                 }
-                if constexpr (ROT == kRotInterTable) {
+                if constexpr (KROT == kRotInterTable) {
                     kc2[j] = *reinterpret_cast<const u32x4*>(cg + to + HALF * sizeof(T));
                     ks2[j] = *reinterpret_cast<const u32x4*>(sg + to + HALF * sizeof(T));
                 }
-                if constexpr (rot_gen(ROT)) kpos[j] = Pg[k0 + kap];
+                if constexpr (rot_gen(KROT)) kpos[j] = Pg[k0 + kap];
             }
         }
 #pragma unroll
@@ -294,21 +310,21 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             if (KITEMS % NT == 0 || it < KITEMS) {
                 const int kap = it / KCH, c = (it % KCH) * 8;
                 T* dst = &sK[buf][kprime_row(kap) * KP + c];
-                if constexpr (ROT == kRotHalfTable) {
+                if constexpr (KROT == kRotHalfTable) {
                     u32x4 xo, yo;
                     rotate_pair_packed<T>(kx[j], ky[j], kc[j], ks[j], xo, yo);
                     *reinterpret_cast<u32x4*>(dst) = xo;
                     *reinterpret_cast<u32x4*>(dst + HALF) = yo;
-                } else if constexpr (ROT == kRotInterTable) {
+                } else if constexpr (KROT == kRotInterTable) {
                     *reinterpret_cast<u32x4*>(dst) = rotate_interleaved_packed<T>(kx[j], kc[j], ks[j]);
                     *reinterpret_cast<u32x4*>(dst + HALF) = rotate_interleaved_packed<T>(ky[j], kc2[j], ks2[j]);
-                } else if constexpr (ROT == kRotHalfGen) {
+                } else if constexpr (KROT == kRotHalfGen) {
                     u32x4 cc, ss, xo, yo;
                     gen_table_chunk<T>(kpos[j], a.pos_scale, kf[j], cc, ss);
                     rotate_pair_packed<T>(kx[j], ky[j], cc, ss, xo, yo);
                     *reinterpret_cast<u32x4*>(dst) = xo;
                     *reinterpret_cast<u32x4*>(dst + HALF) = yo;
-                } else if constexpr (ROT == kRotInterGen) {
+                } else if constexpr (KROT == kRotInterGen) {
                     u32x4 cc, ss;
                     gen_table_chunk_inter<T>(kpos[j], a.pos_scale, &kf[j][0], cc, ss);
                     *reinterpret_cast<u32x4*>(dst) = rotate_interleaved_packed<T>(kx[j], cc, ss);
@@ -343,25 +359,25 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     int32_t qpos = 0;
     {
         const T* qp = reinterpret_cast<const T*>(a.q) + sv.qbase + (int64_t)qrow * a.qs[1] + (int64_t)head * a.qs[2];
-        if constexpr (rot_gen(ROT)) qpos = Pg[qrow];
+        if constexpr (rot_gen(QROT)) qpos = Pg[qrow];
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
             const int d = 16 * u + 8 * h;
             qxr[u] = load_chunk<T>(qp + d).w;
             qyr[u] = load_chunk<T>(qp + d + HALF).w;
-            if constexpr (ROT == kRotHalfTable || ROT == kRotInterTable) {
+            if constexpr (QROT == kRotHalfTable || QROT == kRotInterTable) {
                 qcr[u] = load_chunk<T>(Cg + (int64_t)qrow * D + d).w;
                 qsr[u] = load_chunk<T>(Sg + (int64_t)qrow * D + d).w;
             }
-            if constexpr (ROT == kRotInterTable) {
+            if constexpr (QROT == kRotInterTable) {
                 qc2r[u] = load_chunk<T>(Cg + (int64_t)qrow * D + d + HALF).w;
                 qs2r[u] = load_chunk<T>(Sg + (int64_t)qrow * D + d + HALF).w;
             }
-            if constexpr (ROT == kRotHalfGen) {
+            if constexpr (QROT == kRotHalfGen) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qf[u][e] = Fg[d + e];
             }
-            if constexpr (ROT == kRotInterGen) {
+            if constexpr (QROT == kRotInterGen) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qf[u][e] = Fg[(e < 4 ? d : d + HALF) / 2 + (e & 3)];
             }
@@ -374,12 +390,12 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             float x[8], y[8];
             unpack<T>(Chunk8<T>{qxr[u]}, x);
             unpack<T>(Chunk8<T>{qyr[u]}, y);
-            if constexpr (ROT == kRotHalfTable) {
+            if constexpr (QROT == kRotHalfTable) {
                 float c[8], s[8];
                 unpack<T>(Chunk8<T>{qcr[u]}, c);
                 unpack<T>(Chunk8<T>{qsr[u]}, s);
                 rotate_pair(x, y, c, s, c, s);
-            } else if constexpr (ROT == kRotInterTable) {
+            } else if constexpr (QROT == kRotInterTable) {
                 float c0[8], s0[8], c1[8], s1[8];
                 unpack<T>(Chunk8<T>{qcr[u]}, c0);
                 unpack<T>(Chunk8<T>{qsr[u]}, s0);
@@ -387,14 +403,14 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 unpack<T>(Chunk8<T>{qs2r[u]}, s1);
                 rotate_interleaved(x, c0, s0);
                 rotate_interleaved(y, c1, s1);
-            } else if constexpr (ROT == kRotHalfGen) {
+            } else if constexpr (QROT == kRotHalfGen) {
                 float c[8], s[8];
                 u32x4 cc, ss;
                 gen_table_chunk<T>(qpos, a.pos_scale, qf[u], cc, ss);
                 unpack<T>(Chunk8<T>{cc}, c);
                 unpack<T>(Chunk8<T>{ss}, s);
                 rotate_pair(x, y, c, s, c, s);
-            } else if constexpr (ROT == kRotInterGen) {
+            } else if constexpr (QROT == kRotInterGen) {
                 float c0[8], s0[8], c1[8], s1[8];
                 u32x4 cc, ss;
                 gen_table_chunk_inter<T>(qpos, a.pos_scale, &qf[u][0], cc, ss);
@@ -446,7 +462,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
         auto gen_finish = [&](int e) {
             if constexpr (kGenSliced) {
                 rope_sincos_b(gk, gr2, gsr, gsv[e], gcv[e]);
-                if constexpr (ROT == kRotHalfGen) {
+                if constexpr (KROT == kRotHalfGen) {
                     if (e & 1) {
                         kc[0][e >> 1] = Elem<T>::pack(gcv[e - 1], gcv[e]);
                         ks[0][e >> 1] = Elem<T>::pack(gsv[e - 1], gsv[e]);
@@ -570,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             // staged tile's table values here in one piece (rounded to T as rope_tables_ex
             // stores them, like the pieces above)
             if (!active || __builtin_amdgcn_ballot_w64(gfar) != 0) {
-                if constexpr (ROT == kRotHalfGen) {
+                if constexpr (KROT == kRotHalfGen) {
                     gen_table_chunk<T>(kpos[0], a.pos_scale, kf[0], kc[0], ks[0]);
                 } else {
                     gen_table_chunk_inter<T>(kpos[0], a.pos_scale, &kf[0][0], kc[0], ks[0]);
@@ -578,7 +594,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 }
             }
         }
-        constexpr bool kSliced = ROT != kRotNone && NKI == 1 && KITEMS == NT && D == 128;
+        constexpr bool kSliced = KROT != kRotNone && NKI == 1 && KITEMS == NT && D == 128;
         if constexpr (kSliced) {
             // ---- O^T += V^T P^T, each MFMA followed by a slice of the next tile's K rotation
             // (vector work the matrix core does not wait for); the P.V of inactive waves
@@ -599,7 +615,7 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             float rx0 = 0.f, rx1 = 0.f, ry0 = 0.f, ry1 = 0.f, rc0 = 0.f, rc1 = 0.f, rs0 = 0.f, rs1 = 0.f;
             u32x4 kxo, kyo;
             auto rot_slice = [&](int sl) {
-                if constexpr (rot_inter(ROT)) {
+                if constexpr (rot_inter(KROT)) {
                     // word w of the x half (w < 4) or of the y half: unpack, then rotate and pack
                     const int w = sl >> 1;
                     const u32x4& src = w < 4 ? kx[0] : ky[0];
@@ -953,6 +969,18 @@ inline void launch16(const FaArgs& a, int rot, dim3 grid, hipStream_t stream) {
             break;
         case kRotInterGen:
             hipLaunchKernelGGL((flash_fwd16_kernel<T, D, HP, kRotInterGen>), grid, dim3(512), 0, stream, a);
+            break;
+        case kRotQHalfTable:
+            hipLaunchKernelGGL((flash_fwd16_kernel<T, D, HP, kRotQHalfTable>), grid, dim3(512), 0, stream, a);
+            break;
+        case kRotQInterTable:
+            hipLaunchKernelGGL((flash_fwd16_kernel<T, D, HP, kRotQInterTable>), grid, dim3(512), 0, stream, a);
+            break;
+        case kRotQHalfGen:
+            hipLaunchKernelGGL((flash_fwd16_kernel<T, D, HP, kRotQHalfGen>), grid, dim3(512), 0, stream, a);
+            break;
+        case kRotQInterGen:
+            hipLaunchKernelGGL((flash_fwd16_kernel<T, D, HP, kRotQInterGen>), grid, dim3(512), 0, stream, a);
             break;
     }
 }

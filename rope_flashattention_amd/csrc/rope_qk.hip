@@ -8,6 +8,8 @@
 // blog] (section 二) measures as pure data movement, so the kernel is HBM bound:
 // it reads q and k, writes q' and k', and reads each table row once per block of heads
 // (or forms the row's values in the kernel from positions and inverse frequencies).
+// The same kernel with q's heads left out is the fused attention's k' pre-pass (k' rows
+// written once per key into a packed workspace).
 //
 // Thread mapping: one thread owns one token and one 8-column chunk j of the first half
 // together with chunk j + D/2 (for the rotate-half pairing the two are partners; for the
@@ -31,7 +33,8 @@ struct QkArgs {
     const float* inv_freq;
     const int32_t* cu_seqlens;
     int64_t qs[3];  // {batch, token, head} strides in elements (q and out_q)
-    int64_t ks[3];  // (k and out_k)
+    int64_t ks[3];  // k
+    int64_t oks[3]; // out_k (equal to ks for rope_qk; the packed k' rows for the attention pre-pass)
     int32_t varlen;
     int32_t seqlen;         // dense: tokens per sequence
     int32_t rows;           // token rows processed: dense batch*seqlen, varlen ntokens
@@ -41,6 +44,7 @@ struct QkArgs {
     int32_t table_seq_rows; // dense: 0 = shared table
     int32_t heads_per_block;
     int32_t inv_freq_rows;
+    int32_t half_cols;      // rotate-half tables: columns [0, D/2) read and applied to both halves
     float pos_scale;
 };
 
@@ -57,6 +61,14 @@ __device__ __forceinline__ void qk_table_values(const QkArgs& a, int64_t trow, i
         const T* srow = reinterpret_cast<const T*>(a.sin) + trow * D;
         unpack<T>(load_chunk<T>(crow + j), c0);
         unpack<T>(load_chunk<T>(srow + j), s0);
+        if (PAIR == ROPE_PAIR_HALF && a.half_cols) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                c1[e] = c0[e];
+                s1[e] = s0[e];
+            }
+            return;
+        }
         unpack<T>(load_chunk<T>(crow + j + half), c1);
         unpack<T>(load_chunk<T>(srow + j + half), s1);
         return;
@@ -146,11 +158,12 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(QkArgs a) {
     }
 
     // token -> (sequence, position) offsets and table row
-    int64_t qoff, koff, trow;
+    int64_t qoff, koff, kooff, trow;
     int b = 0;
     if (a.varlen) {
         qoff = (int64_t)t * a.qs[1];
         koff = (int64_t)t * a.ks[1];
+        kooff = (int64_t)t * a.oks[1];
         trow = t;
         if (GEN && a.inv_freq_rows > 1) {
             // sequence of packed token t (batch <= ROPE_MAX_BATCH here)
@@ -162,6 +175,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(QkArgs a) {
         const int s = t - b * a.seqlen;
         qoff = (int64_t)b * a.qs[0] + (int64_t)s * a.qs[1];
         koff = (int64_t)b * a.ks[0] + (int64_t)s * a.ks[1];
+        kooff = (int64_t)b * a.oks[0] + (int64_t)s * a.oks[1];
         trow = (a.table_seq_rows ? (int64_t)b * a.table_seq_rows : 0) + s;
     }
     float c0[8], s0[8], c1[8], s1[8];
@@ -172,7 +186,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(QkArgs a) {
         const int h = isq ? hh : hh - a.hq;
         const int64_t off = isq ? qoff + (int64_t)h * a.qs[2] : koff + (int64_t)h * a.ks[2];
         src = reinterpret_cast<const T*>(isq ? a.q : a.k) + off;
-        dst = reinterpret_cast<T*>(isq ? a.oq : a.ok) + off;
+        dst = isq ? reinterpret_cast<T*>(a.oq) + off : reinterpret_cast<T*>(a.ok) + kooff + (int64_t)h * a.oks[2];
     };
     auto rotate_store = [&](const Chunk8<T>& xc, const Chunk8<T>& yc, T* dst) {
         float x[8], y[8];
@@ -252,12 +266,14 @@ static void launch_qk_typed(const QkArgs& a, int pairing, bool gen, bool nt, boo
            : launch_qk_mode<T, false, false>(a, pairing, gen, grid, stream);
 }
 
-hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
+// hq heads of q (0: k only) and the hkv heads of k; out_k rows at strides oks.
+static hipError_t launch_qk(const rope_attn_params* p, int hq, void* ok, const int64_t oks[3], bool half_cols,
+                            hipStream_t stream) {
     QkArgs a;
     a.q = p->q;
     a.k = p->k;
     a.oq = p->out_q;
-    a.ok = p->out_k;
+    a.ok = ok;
     a.cos = p->cos;
     a.sin = p->sin;
     a.pos = p->pos;
@@ -266,22 +282,24 @@ hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
     for (int i = 0; i < 3; ++i) {
         a.qs[i] = p->q_stride[i];
         a.ks[i] = p->k_stride[i];
+        a.oks[i] = oks[i];
     }
+    a.half_cols = half_cols ? 1 : 0;
     a.varlen = p->cu_seqlens != nullptr;
     a.seqlen = p->seqlen;
     a.rows = a.varlen ? p->ntokens : p->batch * p->seqlen;
     a.batch = p->batch;
-    a.hq = p->hq;
+    a.hq = hq;
     a.hkv = p->hkv;
     a.head_dim = p->head_dim;
     a.table_seq_rows = p->table_seq_rows;
     a.inv_freq_rows = p->inv_freq_rows;
     a.pos_scale = p->pos_scale;
     const bool gen = p->cos == nullptr;
-    const int heads = p->hq + p->hkv;
+    const int heads = hq + p->hkv;
     const int chunks = p->head_dim / 16;
     // heads contiguous within a token (BSND, packed TND): one thread per (token, head, chunk)
-    const bool hi = p->q_stride[2] < p->q_stride[1] && p->k_stride[2] < p->k_stride[1] &&
+    const bool hi = (hq == 0 || p->q_stride[2] < p->q_stride[1]) && p->k_stride[2] < p->k_stride[1] &&
                     ((int64_t)a.rows * heads * chunks + 255) / 256 <= (int64_t)INT32_MAX;
     dim3 grid;
     if (hi) {
@@ -305,6 +323,21 @@ hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_rope_qk(const rope_attn_params* p, hipStream_t stream) {
+    return launch_qk(p, p->hq, p->out_k, p->k_stride, false, stream);
+}
+
+// The attention pre-pass: k' of every key row and kv head into kout, head-major (dense
+// [batch, hkv, seqlen, D], varlen [hkv, ntokens, D], so that a key tile is one contiguous
+// block), with the fused kernel's table use (rotate-half tables: columns [0, D/2) only), so
+// k' equals what its in-loop rotation stages.
+hipError_t launch_rope_k_prepass(const rope_attn_params* p, void* kout, hipStream_t stream) {
+    const int64_t D = p->head_dim;
+    const int64_t plane = (p->cu_seqlens ? (int64_t)p->ntokens : (int64_t)p->seqlen) * D;
+    const int64_t oks[3] = {p->cu_seqlens ? 0 : (int64_t)p->hkv * plane, D, plane};
+    return launch_qk(p, 0, kout, oks, true, stream);
 }
 
 }  // namespace ropefa

@@ -1,0 +1,178 @@
+"""GPU tests of rope_flash_attn_fwd_ws: the fused forward with k' written once per key by a
+pre-pass (q still rotated in registers) against the same call with K rotated in every
+workgroup that stages it (rope_flash_attn_fwd).
+
+Both paths round k' the same way (float32 products, one rounding to the 16-bit type, the
+rotate-half path reading table columns [0, D/2) only) and then run the same matrix and
+softmax steps in the same order, so O and lse must be equal bit for bit; one case per
+table mode is also held against the fp64 oracle at the attention bars.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import rope_flashattention_amd as rfa
+from rope_flashattention_amd import workloads as wl
+from gpu_common import ATTN_TOL, device, packed_out, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def tables(inp, pairing, per_token):
+    w = inp.workload
+    dev = device()
+    D = w.head_dim
+    if not w.varlen and not per_token:
+        f = torch.from_numpy(rfa.inv_freq(w.base, D, [w.seqlen], w.trained_len)).to(dev)
+        pos = torch.from_numpy(inp.pos[: w.seqlen]).to(dev)
+        s, c = rfa.rope_tables(pos, f, [w.seqlen], D, w.pos_scale, w.torch_dtype, pairing=pairing)
+        return s, c, pos, f, 0
+    f = torch.from_numpy(rfa.inv_freq(w.base, D, inp.seq_lens, w.trained_len)).to(dev)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    s, c = rfa.rope_tables(pos, f, inp.seq_lens, D, w.pos_scale, w.torch_dtype, pairing=pairing)
+    return s, c, pos, f, (0 if w.varlen else w.seqlen)
+
+
+def run_both(inp, pairing="half", formed=False, layout="BNSD", per_token=False, causal=None):
+    """(in-loop O, lse), (pre-pass O, lse) and the pre-pass workspace size."""
+    w = inp.workload
+    dev = device()
+    lay = "TND" if w.varlen else layout
+    q, k, v = to_dev(inp, lay)
+    s, c, pos, f, tsr = tables(inp, pairing, per_token)
+    kw = dict(causal=w.causal if causal is None else causal, softmax_scale=w.softmax_scale, table_seq_rows=tsr,
+              pairing=pairing, layout=lay)
+    if w.varlen:
+        kw.update(cu_seqlens=torch.from_numpy(wl.cu_seqlens(inp.seq_lens)).to(dev),
+                  max_seqlen=int(inp.seq_lens.max()))
+    if formed:
+        args = (q, k, v, None, None)
+        kw.update(pos=pos, inv_freq=f, pos_scale=w.pos_scale)
+    else:
+        args = (q, k, v, c, s)
+    need = rfa.flash_attn_fwd_workspace_size(*args, **{x: kw[x] for x in kw if x not in ("softmax_scale",)})
+    ref = rfa.rope_flash_attn_fwd(*args, workspace=None, return_lse=True, **kw)
+    ws = torch.empty(need + 4096, dtype=torch.uint8, device=dev)
+    got = rfa.rope_flash_attn_fwd(*args, workspace=ws, return_lse=True, **kw)
+    auto = rfa.rope_flash_attn_fwd(*args, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return ref, got, auto, need
+
+
+def equal(a, b):
+    return torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def oracle_check(inp, o, lse, pairing="half", layout="BNSD", causal=None):
+    w = inp.workload
+    qn, kn, vn = inp.packed()
+    fr = orc.inv_freq_per_sequence(w.base, inp.seq_lens, w.head_dim, w.trained_len)
+    rs, rc = orc.rope_tables(inp.pos, fr, inp.seq_lens, w.pos_scale, "fp32", pairing)
+    rs, rc = orc.round_rne(rs, w.dtype), orc.round_rne(rc, w.dtype)
+    ro, rl = orc.rope_attention(qn, kn, vn, rc, rs, inp.seq_lens, w.softmax_scale,
+                                w.causal if causal is None else causal, pairing)
+    err = np.abs(packed_out(inp, o, "TND" if w.varlen else layout) - ro).max()
+    lerr = np.abs(lse.cpu().numpy().astype(np.float64) - rl).max()
+    return err, lerr
+
+
+CASES = {
+    # GQA 8:1 (8 q heads per workgroup, 32 query rows): 16 query tiles reach the first key
+    "bf16 GQA H16/2 D128 S500": wl.Workload("bf16 GQA H16/2 D128 S500", "bf16", 2, 16, 2, 128, seqlen=500,
+                                            base=1e4, seed=7101),
+    "f16 GQA H16/2 D128 S500": wl.Workload("f16 GQA H16/2 D128 S500", "f16", 2, 16, 2, 128, seqlen=500,
+                                           base=1e4, seed=7102),
+    "bf16 GQA H16/2 D64 S501": wl.Workload("bf16 GQA H16/2 D64 S501", "bf16", 1, 16, 2, 64, seqlen=501, base=1e4,
+                                          seed=7103),
+    "f16 GQA H32/4 D128 S1000 s=2": wl.Workload("f16 GQA H32/4 D128 S1000 s=2", "f16", 1, 32, 4, 128,
+                                                seqlen=1000, base=1e6, pos_scale=2.0, seed=7104),
+    # MHA, 256 query rows per workgroup: S3900 gives 8.5 rotations per key in-loop
+    "bf16 MHA H2/2 D128 S3900": wl.Workload("bf16 MHA H2/2 D128 S3900", "bf16", 1, 2, 2, 128, seqlen=3900,
+                                            base=1e4, seed=7105),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_prepass_equals_in_loop(name, pairing):
+    inp = wl.generate(CASES[name])
+    ref, got, auto, need = run_both(inp, pairing)
+    same = equal(ref, got) and equal(ref, auto)
+    say(f"{name} {pairing}: workspace {need} bytes, pre-pass == in-loop: {same}")
+    assert need > 0 and same
+    if name.startswith("bf16 GQA H16/2"):
+        err, lerr = oracle_check(inp, got[0], got[1], pairing)
+        say(f"  vs oracle: max-abs {err:.3e} lse {lerr:.3e}")
+        assert err <= ATTN_TOL["bf16"] and lerr <= ATTN_TOL["bf16"]
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prepass_formed_tables(pairing, D):
+    w = wl.Workload(f"formed GQA H16/2 D{D} S520", "bf16", 2, 16, 2, D, seqlen=520, base=5e5, pos_scale=2.0,
+                    seed=7110 + D)
+    inp = wl.generate(w)
+    ref, got, auto, need = run_both(inp, pairing, formed=True)
+    # the formed-table result also equals the read-table call (pre-pass on both)
+    _, tab, _, _ = run_both(inp, pairing)
+    same = equal(ref, got) and equal(ref, auto) and equal(got, tab)
+    say(f"formed D{D} {pairing}: workspace {need}, equal: {same}")
+    assert need > 0 and same
+
+
+def test_prepass_varlen_per_token_tables():
+    """Packed sequences with per-sequence NTK frequencies (per-token tables), including a
+    length-1 sequence and ragged tails; max_seqlen sets the plan."""
+    w = wl.Workload("varlen GQA H16/2 D128", "f16", 5, 16, 2, 128, varlen=True, len_range=(450, 700), base=1e4,
+                    trained_len=256, seed=7120)
+    inp0 = wl.generate(w)
+    lens = inp0.seq_lens.copy()
+    lens[1] = 1
+    T = int(lens.sum())
+    inp = wl.Inputs(w, inp0.q[:T].contiguous(), inp0.k[:T].contiguous(), inp0.v[:T].contiguous(), lens,
+                    np.concatenate([np.arange(L, dtype=np.int32) for L in lens]))
+    ref, got, auto, need = run_both(inp)
+    same = equal(ref, got) and equal(ref, auto)
+    err, lerr = oracle_check(inp, got[0], got[1])
+    say(f"varlen lens {inp.seq_lens.tolist()}: workspace {need}, equal: {same}, max-abs {err:.3e} lse {lerr:.3e}")
+    assert need > 0 and same and err <= ATTN_TOL["f16"] and lerr <= ATTN_TOL["f16"]
+
+
+def test_prepass_bsnd_per_sequence_tables_and_non_causal():
+    w = wl.Workload("BSND GQA H16/2 D128 S480", "bf16", 3, 16, 2, 128, seqlen=480, base=1e4, seed=7130)
+    inp = wl.generate(w)
+    ref, got, auto, need = run_both(inp, layout="BSND", per_token=True)
+    same = equal(ref, got) and equal(ref, auto)
+    ref2, got2, auto2, need2 = run_both(inp, layout="BSND", per_token=True, causal=False)
+    same2 = equal(ref2, got2) and equal(ref2, auto2)
+    err, lerr = oracle_check(inp, got2[0], got2[1], layout="BSND", causal=False)
+    say(f"BSND causal: workspace {need} equal {same}; non-causal: workspace {need2} equal {same2}, "
+        f"max-abs {err:.3e} lse {lerr:.3e}")
+    assert need > 0 and need2 > 0 and same and same2 and err <= ATTN_TOL["bf16"] and lerr <= ATTN_TOL["bf16"]
+
+
+def test_in_loop_when_the_plan_says_so():
+    """Short sequences: no workspace is asked for and the call is rope_flash_attn_fwd."""
+    inp = wl.generate(wl.SMALL[2])
+    ref, got, auto, need = run_both(inp)
+    say(f"{inp.workload.name}: workspace {need}")
+    assert need == 0 and equal(ref, got) and equal(ref, auto)
+
+
+def test_prepass_rejects_small_workspace():
+    inp = wl.generate(CASES["bf16 GQA H16/2 D128 S500"])
+    w = inp.workload
+    q, k, v = to_dev(inp)
+    s, c, _, _, _ = tables(inp, "half", False)
+    need = rfa.flash_attn_fwd_workspace_size(q, k, v, c, s)
+    assert need == 2 * 500 * 2 * 128 * 2
+    small = torch.empty(need - 256, dtype=torch.uint8, device=device())
+    with pytest.raises(rfa.RopeError) as e:
+        rfa.rope_flash_attn_fwd(q, k, v, c, s, softmax_scale=w.softmax_scale, workspace=small)
+    assert e.value.name == "ROPE_ERR_WORKSPACE"

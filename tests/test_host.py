@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(ropelib):
 
 
 def test_abi_version_and_struct_size(ropelib):
-    assert ropelib.rope_abi_version() == 2
+    assert ropelib.rope_abi_version() == 3
     assert ropelib.rope_attn_params_size() == ctypes.sizeof(RopeAttnParams)
     assert ropelib.rope_kv_cache_params_size() == ctypes.sizeof(RopeKvCacheParams)
     assert ropelib.rope_decode_params_size() == ctypes.sizeof(RopeDecodeParams)
@@ -192,6 +192,56 @@ BAD_COMMON = [
 def test_rope_flash_attn_fwd_rejects(ropelib, kw, status):
     p = mutate(valid_params(), **kw)
     assert ropelib.rope_flash_attn_fwd(ctypes.byref(p), None) == ST[status]
+
+
+def fwd_ws_size(ropelib, p):
+    return ropelib.rope_flash_attn_fwd_workspace_size(ctypes.byref(p))
+
+
+def test_fwd_workspace_size(ropelib):
+    """k' pre-pass plan: a workspace of rows x hkv x head_dim 16-bit values (256-byte multiple)
+    once a key would be rotated by at least 8 (query tile, head group) workgroups in-loop."""
+    # GQA 8:1 (8 heads per workgroup, 32 query rows): S448 -> 14 query tiles, 7.5 rotations
+    assert fwd_ws_size(ropelib, valid_params(hq=16, hkv=2, S=448)) == 0
+    # S480 -> 15 query tiles, 8 rotations per key on average (causal)
+    assert fwd_ws_size(ropelib, valid_params(hq=16, hkv=2, S=480)) == 2 * 480 * 2 * 128 * 2
+    # without the mask every query tile reaches every key: S224 -> 7, S250 -> 8
+    assert fwd_ws_size(ropelib, mutate(valid_params(hq=16, hkv=2, S=224), causal=0)) == 0
+    assert fwd_ws_size(ropelib, mutate(valid_params(hq=16, hkv=2, S=250), causal=0)) == \
+        (2 * 250 * 2 * 128 * 2 + 255) // 256 * 256
+    # MHA: one head and 256 query rows per workgroup; S3584 -> 14 tiles, 7.5; S3840 -> 8
+    assert fwd_ws_size(ropelib, valid_params(hq=4, hkv=4, S=3584)) == 0
+    assert fwd_ws_size(ropelib, valid_params(hq=4, hkv=4, S=3840)) == 2 * 3840 * 4 * 128 * 2
+    big = valid_params(hq=64, hkv=8, B=1, S=16384)
+    assert fwd_ws_size(ropelib, big) == 16384 * 8 * 128 * 2
+    assert fwd_ws_size(ropelib, mutate(valid_params(hq=64, hkv=8, B=1, S=16384), cos=None, sin=None)) == 0
+    assert fwd_ws_size(ropelib, mutate(valid_params(hq=64, hkv=8, B=1, S=16384, dtype=3, D=64))) == 0
+    assert fwd_ws_size(ropelib, mutate(valid_params(hq=64, hkv=8, B=1, S=16384), hq=6)) == 0   # invalid
+    # formed tables: pre-pass too, except varlen with per-sequence inverse frequencies
+    gen = mutate(valid_params(hq=64, hkv=8, B=1, S=16384), cos=None, sin=None, pos=FAKE, inv_freq=FAKE,
+                 inv_freq_rows=1, pos_scale=1.0)
+    assert fwd_ws_size(ropelib, gen) == 16384 * 8 * 128 * 2
+    vl = mutate(valid_params(hq=64, hkv=8, B=2, S=0), seqlen=0, cu_seqlens=FAKE, max_seqlen=8000, ntokens=16000,
+                cos=None, sin=None, pos=FAKE, inv_freq=FAKE, inv_freq_rows=1, pos_scale=1.0)
+    for name, H in (("q_stride", 64), ("k_stride", 8), ("v_stride", 8), ("o_stride", 64)):
+        getattr(vl, name)[:] = (0, H * 128, 128, 1)   # packed TND
+    assert fwd_ws_size(ropelib, vl) == 16000 * 8 * 128 * 2
+    vl.inv_freq_rows = 2
+    assert fwd_ws_size(ropelib, vl) == 0
+
+
+@no_gpu_only
+@pytest.mark.parametrize("ws,nbytes", [(None, 1 << 30), (FAKE + 128, 1 << 30), (FAKE, 16384 * 8 * 128 * 2 - 1)])
+def test_fwd_ws_rejects_workspace(ropelib, ws, nbytes):
+    p = valid_params(hq=64, hkv=8, B=1, S=16384)
+    assert ropelib.rope_flash_attn_fwd_ws(ctypes.byref(p), ws, nbytes, None) == ST["ROPE_ERR_WORKSPACE"]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,status", BAD_COMMON[:8])
+def test_fwd_ws_validates_params_first(ropelib, kw, status):
+    p = mutate(valid_params(hq=64, hkv=8, B=1, S=16384), **kw)
+    assert ropelib.rope_flash_attn_fwd_ws(ctypes.byref(p), None, 0, None) == ST[status]
 
 
 @no_gpu_only
