@@ -445,7 +445,13 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
     const int tr_col = ((l >> 4) & 1) * 16 + 4 * (l & 3);
 
     stage_load(0);
+    // q's loads were issued before the first tile's, so the rotation waits for them only and
+    // runs while the tile is still in flight (the compiler would otherwise sink it below the
+    // barrier, into the critical path before the first MFMA)
     rotate_q();
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) asm volatile("" ::"v"(qreg[u]));
+    __builtin_amdgcn_sched_barrier(0);
     stage_store(0);
     if (n_kt > 1) stage_load(1);
     __syncthreads();
