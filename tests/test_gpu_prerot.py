@@ -176,3 +176,14 @@ def test_prepass_rejects_small_workspace():
     with pytest.raises(rfa.RopeError) as e:
         rfa.rope_flash_attn_fwd(q, k, v, c, s, softmax_scale=w.softmax_scale, workspace=small)
     assert e.value.name == "ROPE_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_prepass_equals_in_loop_full_size(cfg):
+    """The full workloads whose plan takes the pre-pass: the in-loop call gives the same bits,
+    so the full-size oracle parity of the pre-pass call (test_gpu_full_size) covers both."""
+    inp = wl.generate(wl.CONFIGS[cfg])
+    ref, got, auto, need = run_both(inp)
+    same = equal(ref, got) and equal(ref, auto)
+    say(f"cfg{cfg} {inp.workload.name}: workspace {need} bytes, pre-pass == in-loop: {same}")
+    assert need > 0 and same
