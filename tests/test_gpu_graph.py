@@ -97,3 +97,62 @@ def test_graph_replay_matches_eager():
         same = [torch.equal(a, b) for a, b in zip(got, ref)]
         say(f"replay {rep}: out, dq, dk, dv, k_cache, v_cache, decode out, lse equal to eager: {same}")
         assert all(same)
+
+
+def test_graph_replay_prepass_forward():
+    """The forward with the k' pre-pass (two launches into a caller workspace) captured with the
+    table pass; every replay equals the eager call and the in-loop call bit for bit."""
+    dev = device()
+    w = dataclasses.replace(wl.SMALL[5], seed=6200)  # GQA 8:1, S520: the plan takes the pre-pass
+    inp = wl.generate(w)
+    D = w.head_dim
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    f = torch.from_numpy(rfa.inv_freq(w.base, D, [w.seqlen], w.trained_len)).to(dev)
+    pos = torch.arange(w.seqlen, dtype=torch.int32, device=dev)
+    lens = np.array([w.seqlen], dtype=np.int32)
+    sin = torch.empty((w.seqlen, D), dtype=w.torch_dtype, device=dev)
+    cos = torch.empty_like(sin)
+    rfa.rope_tables(pos, f, lens, D, w.pos_scale, w.torch_dtype, sin, cos)
+    need = rfa.flash_attn_fwd_workspace_size(q, k, v, cos, sin)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.hq, inp.ntokens), dtype=torch.float32, device=dev)
+
+    def step():
+        rfa.rope_tables(pos, f, lens, D, w.pos_scale, w.torch_dtype, sin, cos)
+        o, l = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, softmax_scale=w.softmax_scale, out=out, return_lse=True,
+                                       workspace=ws)
+        lse.copy_(l)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    io, il = rfa.rope_flash_attn_fwd(q, k, v, cos, sin, softmax_scale=w.softmax_scale, return_lse=True,
+                                     workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(io, ref_o) and torch.equal(il, ref_l)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    junk = torch.randn(1024, 1024, device=dev)
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        ws.zero_()
+        junk = junk @ junk.T / 1024.0  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        say(f"pre-pass forward replay {rep}: out and lse equal to eager: {same}")
+        assert same
