@@ -679,10 +679,6 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
             }
             if (kt + 2 < n_kt) stage_load(kt + 2);
         } else {
-        // ---- stage the next tile (rotate K) into the other buffer, prefetch the one after
-        if (kt + 1 < n_kt) stage_store(buf ^ 1);
-        if (kt + 2 < n_kt) stage_load(kt + 2);
-
         if (active) {
             // ---- O^T += V^T P^T: product j updates O block j % NMB with key step j / NMB
             // (the D/32 accumulator chains interleaved), operands read three products ahead
@@ -707,6 +703,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // ---- stage the next tile (rotate K) into the other buffer, prefetch the one after,
+        // while the P.V products run
+        if (kt + 1 < n_kt) stage_store(buf ^ 1);
+        if (kt + 2 < n_kt) stage_load(kt + 2);
         }
         __syncthreads();
     }
