@@ -503,6 +503,19 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 }
             }
         };
+        // the first P.V operands of the unsliced path (below) are read right after the score
+        // MFMAs, so their LDS round trip runs under the softmax
+        constexpr bool kSlicedPV = KROT != kRotNone && NKI == 1 && KITEMS == NT && D == 128;
+        constexpr int NMBV = D / 32, PDV = 3;
+        const T* vpv0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
+        auto rd_v0 = [&](int j) {
+            const int kstep = j / NMBV;
+            const T* vp = vpv0 + ((kstep >> 1) * 32 + 8 * (kstep & 1)) * VP + (j % NMBV) * 32;
+            const i16x4 lo = lds_read_tr16(vp);
+            const i16x4 hi = lds_read_tr16(vp + 4 * VP);
+            return __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        vec vpre[PDV];
         if (active) {
             // ---- S^T - m = K' Q'^T - m : lane (r, h) gets keys k0 + 32*blk + 16h + i of query qi
             f32x16 sacc[2];
@@ -524,6 +537,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 gen_finish(7);
+            }
+            if constexpr (!kSlicedPV) {
+#pragma unroll
+                for (int j = 0; j < PDV; ++j) vpre[j] = rd_v0(j);
             }
             // ---- masks: causal (key > query) and the ragged end of the sequence: key
             // k0 + 32*blk + 16h + i is dropped iff it exceeds this lane's last key kmax
@@ -682,22 +699,14 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
         if (active) {
             // ---- O^T += V^T P^T: product j updates O block j % NMB with key step j / NMB
             // (the D/32 accumulator chains interleaved), operands read three products ahead
-            constexpr int NMB = D / 32, NJ = 4 * NMB, PD = 3;
-            const T* vp0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
-            auto rd_v = [&](int j) {
-                const int kstep = j / NMB;
-                const T* vp = vp0 + ((kstep >> 1) * 32 + 8 * (kstep & 1)) * VP + (j % NMB) * 32;
-                const i16x4 lo = lds_read_tr16(vp);
-                const i16x4 hi = lds_read_tr16(vp + 4 * VP);
-                return __builtin_bit_cast(vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            };
+            constexpr int NMB = NMBV, NJ = 4 * NMB, PD = PDV;
             vec vb[PD + 1];
 #pragma unroll
-            for (int j = 0; j < PD; ++j) vb[j] = rd_v(j);
+            for (int j = 0; j < PD; ++j) vb[j] = vpre[j];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                if (j + PD < NJ) vb[(j + PD) % (PD + 1)] = rd_v(j + PD);
+                if (j + PD < NJ) vb[(j + PD) % (PD + 1)] = rd_v0(j + PD);
                 const int kstep = j / NMB;
                 oacc[j % NMB] = Mfma<T>::run(vb[j % (PD + 1)], pk[kstep >> 1][kstep & 1], oacc[j % NMB]);
                 __builtin_amdgcn_sched_barrier(0);
