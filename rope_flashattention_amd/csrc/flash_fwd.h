@@ -503,9 +503,8 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 }
             }
         };
-        // the first P.V operands of the unsliced path (below) are read right after the score
-        // MFMAs, so their LDS round trip runs under the softmax
-        constexpr bool kSlicedPV = KROT != kRotNone && NKI == 1 && KITEMS == NT && D == 128;
+        // the first P.V operands are read right after the score MFMAs, so their LDS round
+        // trip runs under the softmax
         constexpr int NMBV = D / 32, PDV = 3;
         const T* vpv0 = &sV[buf][(16 * h + tr_row) * VP + tr_col];
         auto rd_v0 = [&](int j) {
@@ -538,10 +537,8 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                 }
                 gen_finish(7);
             }
-            if constexpr (!kSlicedPV) {
 #pragma unroll
-                for (int j = 0; j < PDV; ++j) vpre[j] = rd_v0(j);
-            }
+            for (int j = 0; j < PDV; ++j) vpre[j] = rd_v0(j);
             // ---- masks: causal (key > query) and the ragged end of the sequence: key
             // k0 + 32*blk + 16h + i is dropped iff it exceeds this lane's last key kmax
             if ((a.causal && k0 + kBN - 1 > q0) || k0 + kBN > L) {
@@ -670,10 +667,10 @@ __global__ __launch_bounds__(512, 1) void flash_fwd16_kernel(FaArgs a) {
                                            __builtin_fmaf(ry1, rc1, __fmul_rn(rx1, rs1)));
                 }
             };
-            constexpr int PD = 3;
+            constexpr int PD = PDV;
             vec vb[PD + 1];
 #pragma unroll
-            for (int j = 0; j < PD; ++j) vb[j] = rd_v(j);
+            for (int j = 0; j < PD; ++j) vb[j] = vpre[j];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
