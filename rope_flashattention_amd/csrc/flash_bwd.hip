@@ -760,6 +760,18 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 sacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&ka[off]), qb[s], sacc);
                 dpacc = BMma<T>::run(*reinterpret_cast<const u32x4*>(&va[off]), db[s], dpacc);
             }
+            // the K'^T operands of the first dQ' products, read now so that their LDS round trips
+            // run under the exponentials below (all of them: the registers spill)
+            auto rd_kt = [&](int mb, int s) {
+                const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
+                const int e = mb * 32 + tr_col;
+                const i16x4 lo = bwd_tr16(&ktr[r * PT + e]);
+                const i16x4 hi = bwd_tr16(&ktr[(r + 4) * PT + e]);
+                return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            u32x4 kto[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) kto[s] = rd_kt(0, s);
             const int thr = kmax - (k0 + 32 * blk + 16 * hh);  // key ... + i is masked iff i > thr
             u32x4 dsk[2];
             auto probs = [&](auto masked) {
@@ -785,15 +797,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int r = blk * 32 + 16 * hh + 8 * s + tr_row;
-                    const int e = mb * 32 + tr_col;
-                    const i16x4 lo = bwd_tr16(&ktr[r * PT + e]);
-                    const i16x4 hi = bwd_tr16(&ktr[(r + 4) * PT + e]);
-                    dqacc[mb] = BMma<T>::run(__builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5,
-                                                                                                6, 7)),
-                                             dsk[s], dqacc[mb]);
-                }
+                for (int s = 0; s < 2; ++s) dqacc[mb] = BMma<T>::run(mb == 0 ? kto[s] : rd_kt(mb, s), dsk[s], dqacc[mb]);
         }
     };
     for (int kt = 0; kt < n_kt; kt += 2) {
